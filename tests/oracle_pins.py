@@ -1,0 +1,448 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``check_*`` takes the oracle module (or a stand-in with the same
+functions) and returns a list of failure strings.  The normal tests call them
+on the real oracle and expect no failure; the mutation tests call them on
+copies with a planted mistake and expect at least one failure, which shows
+that the pin would catch that mistake.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_examples.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def f2bits(vals) -> np.ndarray:
+    """Exact float -> bf16 bits for values that are bf16-representable (asserted)."""
+    a = np.asarray(vals, dtype=np.float32)
+    bits = (a.view(np.uint32) >> 16).astype(np.uint16)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(back, a), "value not exact in bf16"
+    return bits
+
+
+def torch_bf16_bits(vals_f32) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(vals_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _fail(out, cond, msg):
+    if not cond:
+        out.append(msg)
+
+
+# --------------------------------------------------------------------------
+def check_bf16_round(o) -> list:
+    """bf16_round against torch's float32 -> bfloat16 conversion (RNE), on
+    structured edge cases and a large random sample of float32 patterns."""
+    out = []
+    rng = np.random.default_rng(7)
+    pats = [rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)]
+    # every exponent, with mantissa tails just below / at / above the tie
+    exps = np.arange(256, dtype=np.uint32) << 23
+    mants = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x10000, 0x18000, 0x7F7FFF,
+                      0x7F8000, 0x7FFFFF, 0x7E8000, 0x3F8000], dtype=np.uint32)
+    grid = (exps[:, None] | mants[None, :]).reshape(-1)
+    pats += [grid, grid | np.uint32(0x80000000)]
+    p = np.concatenate(pats)
+    f = p.view(np.float32)
+    finite = np.isfinite(f)
+    got = o.bf16_round(f[finite].astype(np.float64))
+    ref = torch_bf16_bits(f[finite])
+    bad = np.nonzero(got != ref)[0]
+    _fail(out, bad.size == 0, f"bf16_round differs from torch on {bad.size} finite patterns "
+          f"(first {[hex(int(x)) for x in p[finite][bad[:4]]]})")
+    # infinities and NaN
+    spec = o.bf16_round(np.array([np.inf, -np.inf, np.nan, 0.0, -0.0]))
+    _fail(out, [int(x) for x in spec[[0, 1, 3, 4]]] == [0x7F80, 0xFF80, 0x0000, 0x8000],
+          f"bf16_round special values wrong: {[hex(int(x)) for x in spec]}")
+    _fail(out, (int(spec[2]) & 0x7F80) == 0x7F80 and (int(spec[2]) & 0x7F) != 0, "NaN not kept NaN")
+    # decode is exact: bf16 value -> float64 -> same pattern
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    dec = o.bf16_decode(allb)
+    fin = np.isfinite(dec)
+    _fail(out, np.array_equal(o.bf16_round(dec[fin]), allb[fin]), "decode/round do not round-trip")
+    ref_dec = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    _fail(out, np.array_equal(dec[fin], ref_dec[fin]), "bf16_decode differs from torch")
+    return out
+
+
+def check_bf16_add(o) -> list:
+    """Scatter arithmetic: the oracle's correctly rounded bf16 sum against the
+    float32-add-then-RNE route done by torch, on a random sample of bf16 pairs
+    (including large exponent gaps) plus the hand-computed cases of E4."""
+    out = []
+    rng = np.random.default_rng(11)
+    a = rng.integers(0, 1 << 16, size=1 << 21, dtype=np.uint32).astype(np.uint16)
+    b = rng.integers(0, 1 << 16, size=1 << 21, dtype=np.uint32).astype(np.uint16)
+    # near-equal magnitudes (cancellation and ties) as well
+    b2 = (a.astype(np.int32) + rng.integers(-300, 300, size=a.size)).clip(0, 0xFFFF).astype(np.uint16)
+    b2 ^= np.uint16(0x8000) * (rng.random(a.size) < 0.5).astype(np.uint16)
+    A = np.concatenate([a, a])
+    B = np.concatenate([b, b2])
+    da, db = o.bf16_decode(A), o.bf16_decode(B)
+    ok = np.isfinite(da) & np.isfinite(db)
+    got = o.bf16_round(da[ok] + db[ok])
+    ta = torch.from_numpy(A[ok].view(np.int16)).view(torch.bfloat16).float()
+    tb = torch.from_numpy(B[ok].view(np.int16)).view(torch.bfloat16).float()
+    ref = (ta + tb).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan_ref = np.isnan((ta + tb).numpy())
+    bad = np.nonzero((got != ref) & ~nan_ref)[0]
+    _fail(out, bad.size == 0, f"bf16 add differs from float32 route on {bad.size} pairs")
+    for case in golden()["E4_movement"]["adds"]:
+        s = o.bf16_round(o.bf16_decode(np.array([int(case["a"], 16)], np.uint16))
+                         + o.bf16_decode(np.array([int(case["b"], 16)], np.uint16)))
+        _fail(out, int(s[0]) == int(case["sum"], 16), f"E4 add {case['a']}+{case['b']} -> {hex(int(s[0]))}")
+    return out
+
+
+# --------------------------------------------------------------------------
+def _heads_to_bits(heads):
+    """[H][N] per-head values (head_dim 1) -> bf16 bits [N][H]."""
+    return f2bits(np.asarray(heads, dtype=np.float32).T.copy())
+
+
+def check_exact_hand(o) -> list:
+    out = []
+    g = golden()
+    e1 = g["E1_diagonal_exclusion"]
+    q = f2bits(np.array(e1["q"])[:, None])
+    k = f2bits(np.array(e1["k"])[:, None])
+    for mode, key in ((o.REDUCE_PAPER, "M_paper"), (o.REDUCE_HEADMAX, "M_headmax")):
+        M, I = o.exact_block_scores(q, k, 1, 1, 2, mode)
+        _fail(out, np.array_equal(M, np.array(e1[key])), f"E1 M mode {mode}: {M.tolist()}")
+        _fail(out, np.array_equal(I, np.array(e1["I"])), f"E1 I mode {mode}: {I.tolist()}")
+    mask, kept, nk, th = o.select_mask(np.array(e1["I"], np.float32), o.SELECT_MEAN)
+    _fail(out, mask.tolist() == e1["mean_mask"] and float(th) == e1["mean_threshold"],
+          f"E1 mean select: {mask.tolist()} {th}")
+    e2 = g["E2_head_reduction_order"]
+    q = _heads_to_bits(e2["q_heads"])
+    k = _heads_to_bits(e2["k_heads"])
+    M, I = o.exact_block_scores(q, k, 2, 1, 2, o.REDUCE_PAPER)
+    _fail(out, np.array_equal(M, np.array(e2["M_paper"])) and np.array_equal(I, np.array(e2["I_paper"])),
+          f"E2 paper: {M.tolist()} {I.tolist()}")
+    M, I = o.exact_block_scores(q, k, 2, 1, 2, o.REDUCE_HEADMAX)
+    _fail(out, np.array_equal(M, np.array(e2["M_headmax"])) and np.array_equal(I, np.array(e2["I_headmax"])),
+          f"E2 headmax: {M.tolist()} {I.tolist()}")
+    return out
+
+
+def brute_exact(qf, kf, H, hd, b, mode):
+    """Pure-Python scalar enumeration of Eq. 1/2 (tiny inputs only)."""
+    N = len(qf)
+    nb = N // b
+    c = 1.0 / math.sqrt(hd)
+
+    def S(h, i, j):
+        return sum(qf[i][h * hd + t] * kf[j][h * hd + t] for t in range(hd)) * c
+
+    M = [[0.0] * nb for _ in range(nb)]
+    for n in range(nb):
+        for m in range(nb):
+            pairs = [(i, j) for i in range(n * b, n * b + b) for j in range(m * b, m * b + b) if i != j]
+            if mode == 0:
+                M[n][m] = max(sum(max(0.0, S(h, i, j)) for h in range(H)) / H for i, j in pairs)
+            else:
+                M[n][m] = sum(max(0.0, max(S(h, i, j) for i, j in pairs)) for h in range(H))
+    I = [sum(M[n][m] for n in range(nb)) for m in range(nb)]
+    return np.array(M), np.array(I)
+
+
+def check_exact_bruteforce(o, seeds=range(6)) -> list:
+    out = []
+    for s in seeds:
+        rng = np.random.default_rng(100 + s)
+        H = int(rng.integers(1, 4))
+        hd = int(rng.choice([1, 2, 4]))
+        b = int(rng.choice([2, 4]))
+        nb = int(rng.integers(1, 4))
+        N = nb * b
+        qf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
+        kf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
+        q, k = torch_bf16_bits(qf32), torch_bf16_bits(kf32)
+        qf = o.bf16_decode(q).tolist()
+        kf = o.bf16_decode(k).tolist()
+        for mode in (0, 1):
+            Mb, Ib = brute_exact(qf, kf, H, hd, b, mode)
+            M, I = o.exact_block_scores(q, k, H, hd, b, mode)
+            _fail(out, np.allclose(M, Mb, rtol=1e-12, atol=1e-12) and np.allclose(I, Ib, rtol=1e-12, atol=1e-12),
+                  f"bruteforce seed {s} mode {mode} H{H} hd{hd} b{b} nb{nb}")
+    return out
+
+
+def check_exact_closed_form(o) -> list:
+    """Rank-one scores: Q_i = a e, K_j = beta_j e along one coordinate of every
+    head.  Then every block score of key block m equals
+    a*max_{j in m} beta_j/sqrt(hd) (mode PAPER) or H times that (HEADMAX), for
+    every query block, so I[m] = nb times it."""
+    out = []
+    rng = np.random.default_rng(3)
+    H, hd, b, nb = 3, 8, 4, 5
+    N = nb * b
+    a = 1.5
+    beta = o.bf16_decode(torch_bf16_bits(np.abs(rng.standard_normal(N)).astype(np.float32)))
+    qv = np.zeros((N, H * hd), np.float32)
+    kv = np.zeros((N, H * hd), np.float32)
+    for h in range(H):
+        qv[:, h * hd + 3] = a
+        kv[:, h * hd + 3] = beta
+    q, k = f2bits(qv), f2bits(kv)
+    bm = beta.reshape(nb, b).max(axis=1) * a / math.sqrt(hd)
+    for mode, mult in ((o.REDUCE_PAPER, 1.0), (o.REDUCE_HEADMAX, float(H))):
+        M, I = o.exact_block_scores(q, k, H, hd, b, mode)
+        _fail(out, np.allclose(M, np.tile(bm * mult, (nb, 1)), rtol=1e-13, atol=0),
+              f"closed form M mode {mode}")
+        _fail(out, np.allclose(I, nb * bm * mult, rtol=1e-13, atol=0), f"closed form I mode {mode}")
+    # constant heads of mixed sign: S^h_ij = s_h for every pair, so a head with
+    # negative scores adds nothing; PAPER gives sum_h max(0, s_h) / H and
+    # HEADMAX gives sum_h max(0, s_h), for every block
+    s_h = np.array([1.0, -2.0, 0.5, -0.25])
+    H2, hd2, b2, nb2 = 4, 4, 2, 3
+    qv = np.zeros((nb2 * b2, H2 * hd2), np.float32)
+    kv = np.zeros((nb2 * b2, H2 * hd2), np.float32)
+    for h in range(H2):
+        qv[:, h * hd2] = 2.0
+        kv[:, h * hd2] = s_h[h]       # S = 2 * s_h / sqrt(4) = s_h
+    pos = np.maximum(s_h, 0).sum()
+    for mode, val in ((o.REDUCE_PAPER, pos / H2), (o.REDUCE_HEADMAX, pos)):
+        M, I = o.exact_block_scores(f2bits(qv), f2bits(kv), H2, hd2, b2, mode)
+        _fail(out, np.allclose(M, val, rtol=1e-14, atol=0) and np.allclose(I, nb2 * val, rtol=1e-14, atol=0),
+              f"constant mixed-sign heads, mode {mode}: {M.tolist()}")
+    return out
+
+
+def check_exact_invariants(o) -> list:
+    out = []
+    rng = np.random.default_rng(5)
+    H, hd, b, nb = 3, 16, 8, 6
+    N = nb * b
+    q = torch_bf16_bits(rng.standard_normal((N, H * hd)).astype(np.float32))
+    k = torch_bf16_bits(rng.standard_normal((N, H * hd)).astype(np.float32))
+    Mp, Ip = o.exact_block_scores(q, k, H, hd, b, o.REDUCE_PAPER)
+    Mh, Ih = o.exact_block_scores(q, k, H, hd, b, o.REDUCE_HEADMAX)
+    _fail(out, np.all(H * Mp <= Mh * (1 + 1e-12)), "H*M_paper <= M_headmax violated")
+    _fail(out, np.all(Mp >= 0) and np.all(Mh >= 0), "negative block score")
+    _fail(out, np.any(H * Mp < Mh * (1 - 1e-6)), "the two reductions never differ on random data")
+    # Q -> 2Q is exact in bf16 and doubles every score
+    q2 = torch_bf16_bits(2.0 * o.bf16_decode(q).astype(np.float32))
+    for mode, M0, I0 in ((o.REDUCE_PAPER, Mp, Ip), (o.REDUCE_HEADMAX, Mh, Ih)):
+        M2, I2 = o.exact_block_scores(q2, k, H, hd, b, mode)
+        _fail(out, np.allclose(M2, 2 * M0, rtol=1e-13, atol=0) and np.allclose(I2, 2 * I0, rtol=1e-13, atol=0),
+              f"scaling Q by 2 does not double scores (mode {mode})")
+    # one head: both reductions agree
+    M1p, _ = o.exact_block_scores(q[:, :hd], k[:, :hd], 1, hd, b, o.REDUCE_PAPER)
+    M1h, _ = o.exact_block_scores(q[:, :hd], k[:, :hd], 1, hd, b, o.REDUCE_HEADMAX)
+    _fail(out, np.allclose(M1p, M1h, rtol=1e-13, atol=0), "H=1 reductions differ")
+    # permuting whole blocks of tokens permutes rows and columns of M
+    perm = rng.permutation(nb)
+    rows = (perm[:, None] * b + np.arange(b)[None, :]).reshape(-1)
+    for mode, M0 in ((o.REDUCE_PAPER, Mp), (o.REDUCE_HEADMAX, Mh)):
+        Mq, _ = o.exact_block_scores(q[rows], k[rows], H, hd, b, mode)
+        _fail(out, np.allclose(Mq, M0[np.ix_(perm, perm)], rtol=1e-12, atol=0),
+              f"block permutation not equivariant (mode {mode})")
+    # zero queries: every score is zero
+    Mz, Iz = o.exact_block_scores(np.zeros_like(q), k, H, hd, b, o.REDUCE_PAPER)
+    _fail(out, not Mz.any() and not Iz.any(), "Q = 0 gives non-zero scores")
+    # sub-matrix evaluation agrees with the full matrix
+    Ms, _ = o.exact_block_scores(q, k, H, hd, b, o.REDUCE_PAPER, query_blocks=[4, 1], key_blocks=[2, 4, 0])
+    _fail(out, np.array_equal(Ms, Mp[np.ix_([4, 1], [2, 4, 0])]), "sub-matrix evaluation differs")
+    return out
+
+
+# --------------------------------------------------------------------------
+def check_predictor(o) -> list:
+    out = []
+    e3 = golden()["E3_predictor"]
+    x = f2bits(e3["x"])
+    args = [f2bits(e3[n]) for n in ("u_q", "v_q", "u_k", "v_k")]
+    xbar = o.pool_blocks(x, 2)
+    _fail(out, np.array_equal(o.bf16_decode(xbar), np.array(e3["xbar"])), "E3 xbar")
+    M, I, qh, kh = o.predict_scores(x, *args, 2)
+    _fail(out, np.array_equal(qh, np.array(e3["q_hat"])), f"E3 q_hat {qh.tolist()}")
+    _fail(out, np.array_equal(kh, np.array(e3["k_hat"])), f"E3 k_hat {kh.tolist()}")
+    _fail(out, np.array_equal(M, np.array(e3["M_hat"])), f"E3 M_hat {M.tolist()}")
+    _fail(out, np.array_equal(I, np.array(e3["I_hat"])), f"E3 I_hat {I.tolist()}")
+    # pooling is the block mean: small integers add exactly in float32, and
+    # the mean of 8 integers is exact in bf16 when it is a multiple of 1/8 < 2^5
+    rng = np.random.default_rng(9)
+    b, nb, d = 8, 6, 40
+    xi = rng.integers(-4, 5, size=(nb * b, d)).astype(np.float32)
+    pooled = o.bf16_decode(o.pool_blocks(f2bits(xi), b))
+    _fail(out, np.array_equal(pooled, xi.reshape(nb, b, d).mean(axis=1)), "pooling is not the block mean")
+    # pooled value rounding: an inexact mean is the bf16 rounding of the fp32 mean
+    xr = torch_bf16_bits(rng.standard_normal((nb * b, d)).astype(np.float32))
+    fm = o.bf16_decode(xr).reshape(nb, b, d).astype(np.float32).sum(axis=1, dtype=np.float32)
+    pooled = o.pool_blocks(xr, b)
+    ref = torch_bf16_bits(fm / np.float32(b))
+    _fail(out, np.mean(pooled == ref) > 0.999, "pooled bf16 values disagree with a rounded mean")
+    # X -> 2X: every rounding point scales exactly, so M_hat and I_hat grow 4x
+    r = 16
+    w = [torch_bf16_bits(rng.standard_normal(s).astype(np.float32) / np.sqrt(s[0]))
+         for s in ((d, r), (r, r), (d, r), (r, r))]
+    M1, I1, _, _ = o.predict_scores(xr, *w, b)
+    x2 = torch_bf16_bits(2.0 * o.bf16_decode(xr).astype(np.float32))
+    M2, I2, _, _ = o.predict_scores(x2, *w, b)
+    _fail(out, np.allclose(M2, 4 * M1, rtol=1e-12, atol=0) and np.allclose(I2, 4 * I1, rtol=1e-12, atol=0),
+          "X -> 2X does not scale predicted scores by 4")
+    _fail(out, np.all(M1 >= 0) and np.all(I1 >= 0), "negative predicted score")
+    # a block's predicted column only depends on that block's rows: swapping two
+    # blocks of X swaps the corresponding rows and columns of M_hat
+    rows = np.arange(nb * b).reshape(nb, b)
+    rows[[1, 4]] = rows[[4, 1]]
+    Ms, _, _, _ = o.predict_scores(xr[rows.reshape(-1)], *w, b)
+    p = np.arange(nb)
+    p[[1, 4]] = p[[4, 1]]
+    _fail(out, np.array_equal(Ms, M1[np.ix_(p, p)]), "block swap not equivariant")
+    # brute force on a tiny case
+    bq = _brute_predict(o.bf16_decode(xr[:16, :6]), [o.bf16_decode(a) for a in
+                         (w[0][:6, :4], w[1][:4, :4], w[2][:6, :4], w[3][:4, :4])], 4, o)
+    Mt, It, _, _ = o.predict_scores(xr[:16, :6], w[0][:6, :4], w[1][:4, :4], w[2][:6, :4], w[3][:4, :4], 4)
+    _fail(out, np.allclose(Mt, bq[0], rtol=1e-12, atol=1e-12) and np.allclose(It, bq[1], rtol=1e-12, atol=1e-12),
+          "predictor brute force")
+    return out
+
+
+def _brute_predict(X, W, b, o):
+    """Scalar loops of Eq. 3 with mean pooling; bf16 rounding of the pooled
+    mean and of the hidden ReLU output through torch's conversion."""
+    Uq, Vq, Uk, Vk = W
+    N, d = X.shape
+    nb = N // b
+    r = Uq.shape[1]
+
+    def bf(v):
+        return float(torch.tensor(float(v), dtype=torch.float32).to(torch.bfloat16).float())
+
+    xbar = []
+    for m in range(nb):
+        row = []
+        for c in range(d):
+            acc = np.float32(0)
+            for i in range(b):
+                acc = np.float32(acc + np.float32(X[m * b + i][c]))
+            row.append(bf(np.float32(acc / np.float32(b))))
+        xbar.append(row)
+
+    def pred(U, V):
+        res = []
+        for m in range(nb):
+            hid = [bf(np.float32(max(0.0, sum(xbar[m][c] * U[c][t] for c in range(d))))) for t in range(r)]
+            res.append([sum(hid[t] * V[t][v] for t in range(r)) for v in range(r)])
+        return res
+
+    qh, kh = pred(Uq, Vq), pred(Uk, Vk)
+    M = np.array([[max(0.0, sum(qh[m][v] * kh[n][v] for v in range(r))) for n in range(nb)] for m in range(nb)])
+    return M, M.sum(axis=0)
+
+
+# --------------------------------------------------------------------------
+def check_select(o) -> list:
+    out = []
+    rng = np.random.default_rng(13)
+    s = rng.random(37).astype(np.float32)
+    for kk in (0, 1, 5, 36, 37):
+        mask, kept, nk, th = o.select_mask(s, o.SELECT_TOPK, keep_blocks=kk)
+        ref = np.sort(np.argsort(-s, kind="stable")[:kk])
+        _fail(out, np.array_equal(kept, ref) and nk == kk and int(mask.sum()) == kk, f"topk {kk}")
+        if kk:
+            _fail(out, th == np.sort(s)[::-1][kk - 1], f"topk threshold {kk}")
+    # ties go to the lower block index
+    t = np.array([1, 3, 3, 2, 3, 0], np.float32)
+    _, kept, _, th = o.select_mask(t, o.SELECT_TOPK, keep_blocks=2)
+    _fail(out, kept.tolist() == [1, 2] and th == 3, f"topk ties: {kept.tolist()}")
+    _, kept, _, _ = o.select_mask(t, o.SELECT_TOPK, keep_blocks=4)
+    _fail(out, kept.tolist() == [1, 2, 3, 4], f"topk ties 4: {kept.tolist()}")
+    # NaN sorts last and fails every threshold compare
+    tn = np.array([np.nan, 1, 2, np.nan], np.float32)
+    _, kept, _, _ = o.select_mask(tn, o.SELECT_TOPK, keep_blocks=3)
+    _fail(out, kept.tolist() == [0, 1, 2], f"topk NaN: {kept.tolist()}")
+    mask, _, _, _ = o.select_mask(tn, o.SELECT_THRESHOLD, threshold=0.5)
+    _fail(out, mask.tolist() == [0, 1, 1, 0], "threshold NaN")
+    # threshold: >= keeps ties; extremes keep all / nothing
+    mask, kept, nk, th = o.select_mask(t, o.SELECT_THRESHOLD, threshold=2.0)
+    _fail(out, mask.tolist() == [0, 1, 1, 1, 1, 0] and th == 2.0, "threshold >=")
+    _fail(out, o.select_mask(s, o.SELECT_THRESHOLD, threshold=-1.0)[2] == s.size, "keep-all threshold")
+    _fail(out, o.select_mask(s, o.SELECT_THRESHOLD, threshold=2.0)[2] == 0, "drop-all threshold")
+    # mean: the threshold is the arithmetic mean (exact here: 1/8 multiples)
+    m8 = (rng.integers(0, 64, size=40) / 8.0).astype(np.float32)
+    mask, kept, nk, th = o.select_mask(m8, o.SELECT_MEAN)
+    _fail(out, th == np.float32(np.mean(m8.astype(np.float64))), "mean threshold")
+    _fail(out, np.array_equal(mask.astype(bool), m8 >= th), "mean mask")
+    # random: kept list ascending, counts add up, every kept >= every dropped (topk)
+    mask, kept, nk, th = o.select_mask(s, o.SELECT_TOPK, keep_blocks=11)
+    _fail(out, np.all(np.diff(kept) > 0) and nk + int((mask == 0).sum()) == s.size, "kept list shape")
+    _fail(out, s[mask == 1].min() >= s[mask == 0].max(), "topk order")
+    return out
+
+
+def check_movement(o) -> list:
+    out = []
+    e4 = golden()["E4_movement"]
+    N, b = e4["n_tokens"], e4["block"]
+    mask = np.array(e4["mask"], np.uint8)
+    kept = np.nonzero(mask)[0].astype(np.int32)
+    _fail(out, kept.tolist() == e4["kept_blocks"], "E4 kept list")
+    rng = np.random.default_rng(17)
+    w = 8
+    src = rng.integers(1, 0x7F00, size=(N, w)).astype(np.uint16)
+    sentinel = np.full((10, w), 0xABCD, np.uint16)
+    dst, over = o.gather_pad(src, b, kept, 2, sentinel, e4["pad_multiple"])
+    _fail(out, np.array_equal(dst[:4], src[e4["gathered_rows"]]), "E4 gather rows")
+    _fail(out, not dst[4:8].any(), "E4 pad rows not zero")
+    _fail(out, np.all(dst[8:] == 0xABCD) and not over, "E4 rows past the pad touched")
+    # gather = torch.index_select over the kept token rows
+    N2, b2, w2 = 64, 4, 24
+    src2 = rng.integers(0, 1 << 16, size=(N2, w2)).astype(np.uint16)
+    m2 = (rng.random(N2 // b2) < 0.4).astype(np.uint8)
+    k2 = np.nonzero(m2)[0].astype(np.int32)
+    tok = torch.arange(N2).view(N2 // b2, b2)[torch.from_numpy(k2).long()].reshape(-1)
+    ref = torch.index_select(torch.from_numpy(src2.view(np.int16)), 0, tok).numpy().view(np.uint16)
+    dst2, _ = o.gather_pad(src2, b2, k2, k2.size, np.zeros((N2, w2), np.uint16), 1)
+    _fail(out, np.array_equal(dst2[:tok.numel()], ref) and not dst2[tok.numel():].any(), "gather vs index_select")
+    # capacity: copies past the buffer are dropped and reported
+    small, over = o.gather_pad(src2, b2, k2, k2.size, np.zeros((3, w2), np.uint16), 1)
+    _fail(out, over and np.array_equal(small, ref[:3]) if k2.size * b2 > 3 else True, "capacity overflow")
+    # scatter: keep-all equals the dense bf16 add; drop-all leaves the residual;
+    # only kept rows change; E4 tie rounding
+    res = torch_bf16_bits(rng.standard_normal((N2, w2)).astype(np.float32))
+    yf = torch_bf16_bits(rng.standard_normal((N2, w2)).astype(np.float32))
+    allk = np.arange(N2 // b2, dtype=np.int32)
+    dense = (torch.from_numpy(res.view(np.int16)).view(torch.bfloat16).float()
+             + torch.from_numpy(yf.view(np.int16)).view(torch.bfloat16).float()).to(torch.bfloat16)
+    got = o.scatter_residual(res, b2, allk, allk.size, yf)
+    _fail(out, np.array_equal(got, dense.view(torch.int16).numpy().view(np.uint16)), "keep-all != dense add")
+    _fail(out, np.array_equal(o.scatter_residual(res, b2, allk, 0, yf), res), "drop-all changed the residual")
+    yk = yf[tok.numpy()]
+    got = o.scatter_residual(res, b2, k2, k2.size, yk)
+    dropped = np.ones(N2, bool)
+    dropped[tok.numpy()] = False
+    _fail(out, np.array_equal(got[dropped], res[dropped]), "dropped rows touched")
+    refk = torch.from_numpy(res.view(np.int16)).view(torch.bfloat16).float()
+    refk.index_add_(0, tok, torch.from_numpy(yk.view(np.int16)).view(torch.bfloat16).float())
+    _fail(out, np.array_equal(got, refk.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)),
+          "scatter vs index_add")
+    r0 = np.full((N, 1), 0x3F80, np.uint16)
+    y0 = np.array([[0x3B80], [0x3BC0], [0x3B80], [0x3BC0]], np.uint16)
+    got = o.scatter_residual(r0, b, kept, 2, y0)
+    _fail(out, got[:, 0].tolist() == [0x3F80, 0x3F81, 0x3F80, 0x3F80, 0x3F80, 0x3F81], f"E4 scatter {got[:, 0]}")
+    rc = e4["recompute_by_subtraction"]
+    back = o.bf16_round(o.bf16_decode(np.array([int(rc["stored"], 16)], np.uint16))
+                        - o.bf16_decode(np.array([int(rc["minus"], 16)], np.uint16)))
+    _fail(out, int(back[0]) == int(rc["gives"], 16), "E4 recompute example")
+    return out
+
+
+ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
+              check_exact_closed_form, check_exact_invariants, check_predictor, check_select,
+              check_movement]

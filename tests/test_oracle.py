@@ -1,0 +1,71 @@
+"""The oracle against its pins (hand examples, closed forms, invariants,
+brute force, library routines), and planted mistakes that the pins catch."""
+import importlib.util
+import os
+import types
+
+import pytest
+
+from oracle import lemo_oracle as O
+from tests import oracle_pins as P
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "lemo_oracle.py")
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    failures = check(O)
+    assert not failures, failures
+
+
+def mutant(old: str, new: str):
+    """A copy of the oracle with one planted mistake (text replacement)."""
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+MUTATIONS = [
+    ("no_diagonal_exclusion", "Sbar[same] = -np.inf", "pass", [P.check_exact_hand]),
+    ("headmax_keeps_diagonal", "S[:, same] = -np.inf", "pass", [P.check_exact_bruteforce]),
+    ("transposed_column_sum", "I = M.sum(axis=0) if query_blocks", "I = M.sum(axis=1) if query_blocks",
+     [P.check_exact_hand]),
+    ("no_sqrt_scale", "scale = 1.0 / math.sqrt(head_dim)", "scale = 1.0", [P.check_exact_closed_form]),
+    ("no_head_mean", ".sum(axis=0) / n_heads", ".sum(axis=0)", [P.check_exact_closed_form, P.check_exact_hand]),
+    ("max_before_clamp_swapped", "M[a] = np.maximum(per_head, 0.0).sum(axis=0)", "M[a] = np.maximum(per_head.sum(axis=0), 0.0)",
+     [P.check_exact_closed_form]),
+    ("predictor_no_clamp", "M = np.maximum(q_hat @ k_hat.T, 0.0)", "M = q_hat @ k_hat.T", [P.check_predictor]),
+    ("pool_sum_not_mean", "mean = acc * np.float32(1.0 / block)", "mean = acc", [P.check_predictor]),
+    ("predictor_no_relu", "hid = np.maximum(bf16_decode(xbar) @ bf16_decode(u), 0.0)",
+     "hid = bf16_decode(xbar) @ bf16_decode(u)", [P.check_predictor]),
+    ("predictor_transposed_v", "return bf16_decode(hid_bf16) @ bf16_decode(v)",
+     "return bf16_decode(hid_bf16) @ bf16_decode(v).T", [P.check_predictor]),
+    ("threshold_strict", "keep = s >= theta\n    elif mode == SELECT_MEAN", "keep = s > theta\n    elif mode == SELECT_MEAN",
+     [P.check_select]),
+    ("topk_ties_high_index", "-float(s[c]) if not np.isnan(s[c]) else 0.0, c))",
+     "-float(s[c]) if not np.isnan(s[c]) else 0.0, -c))", [P.check_select]),
+    ("round_truncates", "r = np.rint(np.ldexp(ax, -qexp))", "r = np.floor(np.ldexp(ax, -qexp))",
+     [P.check_bf16_round, P.check_bf16_add]),
+    ("round_ties_away", "r = np.rint(np.ldexp(ax, -qexp))", "r = np.floor(np.ldexp(ax, -qexp) + 0.5)",
+     [P.check_bf16_round]),
+    ("round_no_subnormals", "qexp = np.maximum(e - 8, -133)", "qexp = e - 8", [P.check_bf16_round]),
+    ("gather_wrong_block", "return (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)",
+     "return ((kept[:, None] + 1) * block + np.arange(block)[None, :]).reshape(-1) % 6", [P.check_movement]),
+    ("pad_not_zeroed", "dst[p, :width] = 0", "pass", [P.check_movement]),
+    ("scatter_into_dense_rows", "for p, t in enumerate(rows):", "for p, t in enumerate(range(rows.size)):",
+     [P.check_movement]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,checks", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new, checks):
+    mod = mutant(old, new)
+    failures = []
+    for c in checks:
+        try:
+            failures += c(mod)
+        except Exception as e:  # a crash also counts as caught
+            failures.append(f"{c.__name__} raised {e!r}")
+    assert failures, f"planted mistake {name} went unnoticed"
