@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the token-elimination hot path on one MI355X.
+
+One step = one pass of every stage of the hot path over one synthetic
+Llama2-7B-shaped layer at N = 16384 tokens (d = 4096, 32 heads of 128,
+block 64, predictor rank 128, MLP width 11008), all on one stream with no
+host synchronisation inside the step:
+  1. lemo_block_scores     exact block scores of Q K^T (Eq. 2 head reduction)
+  2. lemo_predict_scores   predicted block scores from X (Eq. 3)
+  3. lemo_select_mask      mean threshold on the predicted scores (Alg. 1 step 1)
+  4. lemo_gather_pad x2    kept rows of X and of the MLP activation, padded to 256
+  5. lemo_scatter_residual layer output of the kept rows added into the residual
+Inputs are generated (seeded, synthetic) and resident in device memory before
+the timed region.  Reported value: tokens scored + eliminated per second.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s scored+eliminated per layer at Llama2-7B N=16K; % MFMA / HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WORKLOAD = "llama2-7b-n16k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_scores_llama2-7b-n16k_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--head-reduce", choices=["paper", "headmax"], default="paper")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "contextual_token_sparsity_amd", "csrc", "block_scores.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the exact-score kernel from committed counter
+    runs, only if they were taken on the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
+              "is described in DESIGN.md and not measured", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from contextual_token_sparsity_amd import lemo, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lemo.lib()
+    w = synth.WORKLOADS[WORKLOAD]
+    N, d, H, hd, b, r, wm = w.n_tokens, w.d_model, w.n_heads, w.head_dim, w.block, w.rank, w.mlp_width
+    nb = N // b
+    mode = lemo.REDUCE_PAPER if args.head_reduce == "paper" else lemo.REDUCE_HEADMAX
+    print(f"[bench] generating {WORKLOAD} inputs", file=sys.stderr, flush=True)
+    L = synth.make_layer(N, d, b, w.seed, n_heads=H, head_dim=hd, rank=r, mlp_width=wm,
+                         planted_frac=w.planted_frac, proj_device="cuda")
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    q, k, x, act = up(L.q), up(L.k), up(L.x), up(L.act)
+    uq, vq, uk, vk = up(L.u_q), up(L.v_q), up(L.u_k), up(L.v_k)
+    resid = x.clone()
+    cap = N                                        # worst case: every block kept
+    y = up(synth.random_bf16(np.random.default_rng(w.seed + 7), (cap, d)))
+    xk = torch.empty((cap, d), dtype=torch.int16, device=dev)
+    ak = torch.empty((cap, wm), dtype=torch.int16, device=dev)
+    I_exact = torch.empty(nb, dtype=torch.float32, device=dev)
+    I_pred = torch.empty(nb, dtype=torch.float32, device=dev)
+    ws_exact = torch.empty(lemo.lemo_block_scores_workspace(N, b), dtype=torch.uint8, device=dev)
+    ws_pred = torch.empty(lemo.lemo_predict_scores_workspace(N, d, b, r), dtype=torch.uint8, device=dev)
+    mask = torch.empty(nb, dtype=torch.uint8, device=dev)
+    kept = torch.empty(nb, dtype=torch.int32, device=dev)
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    theta = torch.empty(1, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = {}
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    def step(timed):
+        if timed:
+            mark("scores0")
+        lemo.lemo_block_scores(q, k, H, hd, b, mode, scores=I_exact, workspace=ws_exact)
+        if timed:
+            mark("scores1")
+        lemo.lemo_predict_scores(x, uq, vq, uk, vk, b, scores=I_pred, workspace=ws_pred)
+        if timed:
+            mark("predict1")
+        lemo.lemo_select_mask(I_pred, lemo.SELECT_MEAN, mask=mask, kept_blocks=kept, n_kept=n_kept,
+                              threshold_used=theta, dev_status=status)
+        if timed:
+            mark("select1")
+        lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256, dev_status=status)
+        lemo.lemo_gather_pad(act, b, kept, n_kept, ak, pad_multiple=256, dev_status=status)
+        if timed:
+            mark("gather1")
+        lemo.lemo_scatter_residual(resid, b, kept, n_kept, y, dev_status=status)
+        if timed:
+            mark("scatter1")
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    host0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - host0
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+
+    def avg(a, b_):
+        return float(np.mean([x.elapsed_time(y_) for x, y_ in zip(ev[a], ev[b_])]))
+
+    stages = {
+        "block_scores": avg("scores0", "scores1"),
+        "predict_scores": avg("scores1", "predict1"),
+        "select_mask": avg("predict1", "select1"),
+        "gather_pad_x_and_act": avg("select1", "gather1"),
+        "scatter_residual": avg("gather1", "scatter1"),
+    }
+    nk = int(n_kept.item())
+    st = int(status.item())
+    flops = 2.0 * N * N * hd * H
+    t_scores_s = stages["block_scores"] * 1e-3
+    achieved = flops / t_scores_s / 1e12
+    R = nk * b
+    Rp = -(-R // 256) * 256
+    move_bytes = 2 * R * d * 2 + (Rp - R) * d * 2 + 2 * R * wm * 2 + (Rp - R) * wm * 2 + 3 * R * d * 2
+    out = {
+        "metric": METRIC,
+        "value": N * args.steps / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama2-7B-shaped layer, N=16384, d=4096, 32 heads x 128, block 64: exact block "
+                        "scores + predictor (rank 128) + mean-threshold select + gather of X and of the MLP "
+                        "activation (11008) padded to 256 + in-place residual add",
+            "n_tokens": N, "d_model": d, "n_heads": H, "head_dim": hd, "block": b, "rank": r,
+            "mlp_width": wm, "head_reduce": args.head_reduce, "select": "mean",
+        },
+        "roofline": {
+            "kernel": "lemo_block_scores (k_block_scores + column sum)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": load_traffic(),
+        },
+        "stages_ms": stages,
+        "n_kept_blocks": nk,
+        "movement_GBps": move_bytes / ((stages["gather_pad_x_and_act"] + stages["scatter_residual"]) * 1e-3) / 1e9,
+        "dev_status": st,
+        "host_wall_s": host_s,
+    }
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(L, w)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(L, w):
+    """The oracle on the host cores, on a bounded sample of one step: exact
+    scores for `s` of the nb query blocks against every key block (scaled up by
+    nb / s), plus the full predictor, select, gather of X and of the MLP
+    activation, and scatter."""
+    from oracle import lemo_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    nb = w.n_blocks
+    s = 8
+    print(f"[bench] cpu baseline: oracle on {s}/{nb} query blocks + full predictor/movement", file=sys.stderr,
+          flush=True)
+    t = time.perf_counter()
+    O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER,
+                         query_blocks=list(range(0, nb, nb // s))[:s])
+    t_exact = (time.perf_counter() - t) * nb / s
+    t = time.perf_counter()
+    _, I_hat, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
+    _, kept, nk, _ = O.select_mask(I_hat.astype(np.float32), O.SELECT_MEAN)
+    R = nk * w.block
+    cap = -(-R // 256) * 256
+    O.gather_pad(L.x, w.block, kept, nk, np.zeros((cap, w.d_model), np.uint16), 256)
+    O.gather_pad(L.act, w.block, kept, nk, np.zeros((cap, w.mlp_width), np.uint16), 256)
+    O.scatter_residual(L.x, w.block, kept, nk, L.y[O.kept_token_rows(kept, nk, w.block)])
+    t_rest = time.perf_counter() - t
+    t_step = t_exact + t_rest
+    return {
+        "value": w.n_tokens / t_step,
+        "unit": "tokens/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"exact scores of {s} of {nb} query blocks (x{nb // s}) + full predictor, mean select, "
+                  f"gathers and scatter; est. step {t_step:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,69 @@
+"""Builds liblemo.so (all HIP sources, gfx950) in-tree with hipcc.
+
+    python -m contextual_token_sparsity_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "liblemo.so")
+SOURCES = ["abi.hip", "block_scores.hip", "predict.hip", "select.hip", "movement.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object, then link the shared library
+    atomically (a running process that has the old library mapped keeps it)."""
+    cc = hipcc()
+    objs = []
+    with tempfile.TemporaryDirectory(prefix="lemo_build_") as tmp:
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        errors = []
+        for src, p in procs:
+            out, _ = p.communicate()
+            noise = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            if p.returncode != 0:
+                errors.append(f"{src}:\n" + "\n".join(noise))
+            elif verbose and noise:
+                print("\n".join(noise))
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,177 @@
+// Host side of the C ABI: argument validation (before anything is enqueued),
+// workspace sizing, status strings and the thread-local error text.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "lemo_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lemo_status fail(lemo_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lemo_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LEMO_OK;
+  return fail(LEMO_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+// Rows of a bf16 matrix: base pointer 16-byte aligned and ld a multiple of 8.
+lemo_status check_rows(const void* p, int ld, int width, const char* name) {
+  REQUIRE(p != nullptr, LEMO_ERR_INVALID_ARG, "%s is NULL", name);
+  REQUIRE(ld >= width, LEMO_ERR_INVALID_ARG, "ld of %s (%d) < width %d", name, ld, width);
+  REQUIRE(aligned16(p) && ld % 8 == 0, LEMO_ERR_ALIGNMENT,
+          "%s must be 16-byte aligned with ld a multiple of 8 (ld=%d)", name, ld);
+  return LEMO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lemo_status_string(lemo_status s) {
+  switch (s) {
+    case LEMO_OK: return "ok";
+    case LEMO_ERR_INVALID_ARG: return "invalid argument";
+    case LEMO_ERR_UNSUPPORTED: return "unsupported shape";
+    case LEMO_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case LEMO_ERR_WORKSPACE: return "workspace missing or too small";
+    case LEMO_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* lemo_last_error(void) { return g_last_error.c_str(); }
+
+int lemo_version(void) { return 100; }  // 0.1.0
+
+size_t lemo_block_scores_workspace(int n_tokens, int block) {
+  if (n_tokens <= 0 || block <= 0 || n_tokens % block) return 0;
+  const size_t nb = (size_t)(n_tokens / block);
+  return lemo_align256(nb * nb * sizeof(float));
+}
+
+lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_tokens, int n_heads, int head_dim,
+                              int ld_q, int ld_k, int block, int head_reduce, float* block_scores, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(scores != nullptr, LEMO_ERR_INVALID_ARG, "scores is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && n_heads > 0 && head_dim > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d n_heads=%d head_dim=%d)", n_tokens, block, n_heads,
+          head_dim);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(head_reduce == LEMO_REDUCE_PAPER || head_reduce == LEMO_REDUCE_HEADMAX, LEMO_ERR_INVALID_ARG,
+          "unknown head_reduce %d", head_reduce);
+  REQUIRE((long long)n_heads * head_dim <= (1LL << 30), LEMO_ERR_INVALID_ARG, "n_heads*head_dim too large");
+  REQUIRE(head_dim == 64 || head_dim == 128, LEMO_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
+  REQUIRE(block == 32 || block == 64 || block == 128, LEMO_ERR_UNSUPPORTED, "block %d (32, 64 or 128 supported)",
+          block);
+  REQUIRE(head_reduce == LEMO_REDUCE_PAPER || n_heads <= 128, LEMO_ERR_UNSUPPORTED,
+          "HEADMAX supports at most 128 heads (got %d)", n_heads);
+  lemo_status st;
+  if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
+  if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
+  float* m_out = block_scores;
+  if (!m_out) {
+    const size_t need = lemo_block_scores_workspace(n_tokens, block);
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    m_out = static_cast<float*>(workspace);
+  }
+  return device_status(lemo_launch_block_scores(q, k, n_tokens, n_heads, head_dim, ld_q, ld_k, block, head_reduce,
+                                                m_out, scores, static_cast<hipStream_t>(stream)),
+                       "lemo_block_scores launch");
+}
+
+size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int rank) {
+  if (n_tokens <= 0 || block <= 0 || n_tokens % block || d_model <= 0 || rank <= 0) return 0;
+  return lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
+}
+
+lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(scores != nullptr && u_q && v_q && u_k && v_k, LEMO_ERR_INVALID_ARG, "scores or a predictor matrix is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && d_model > 0 && rank > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d d_model=%d rank=%d)", n_tokens, block, d_model, rank);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(pow2(block) && block >= 2 && block <= 256, LEMO_ERR_UNSUPPORTED, "block %d (power of two, 2..256)", block);
+  REQUIRE(d_model % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_model %d (multiple of 64 supported)", d_model);
+  REQUIRE(rank % 32 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 32, at most 256)", rank);
+  lemo_status st;
+  if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
+  const size_t need = lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned16(workspace), LEMO_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  return device_status(lemo_launch_predict(x, n_tokens, d_model, ld_x, block, u_q, v_q, u_k, v_k, rank, block_scores,
+                                           scores, workspace, static_cast<hipStream_t>(stream)),
+                       "lemo_predict_scores launch");
+}
+
+lemo_status lemo_select_mask(const float* scores, int n_blocks, int mode, float threshold, int keep_blocks,
+                             uint8_t* mask, int32_t* kept_blocks, int32_t* n_kept, float* threshold_used,
+                             int32_t* dev_status, void* stream) {
+  REQUIRE(scores && mask && kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "scores, mask, kept_blocks or n_kept is NULL");
+  REQUIRE(n_blocks > 0, LEMO_ERR_INVALID_ARG, "n_blocks must be positive (got %d)", n_blocks);
+  REQUIRE(n_blocks <= 8192, LEMO_ERR_UNSUPPORTED, "n_blocks %d (at most 8192)", n_blocks);
+  REQUIRE(mode == LEMO_SELECT_THRESHOLD || mode == LEMO_SELECT_TOPK || mode == LEMO_SELECT_MEAN,
+          LEMO_ERR_INVALID_ARG, "unknown select mode %d", mode);
+  REQUIRE(mode != LEMO_SELECT_TOPK || (keep_blocks >= 0 && keep_blocks <= n_blocks), LEMO_ERR_INVALID_ARG,
+          "keep_blocks %d outside 0..%d", keep_blocks, n_blocks);
+  return device_status(lemo_launch_select(scores, n_blocks, mode, threshold, keep_blocks, mask, kept_blocks, n_kept,
+                                          threshold_used, dev_status, static_cast<hipStream_t>(stream)),
+                       "lemo_select_mask launch");
+}
+
+lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int ld_src, int block,
+                            const int32_t* kept_blocks, const int32_t* n_kept, lemo_bf16* dst, int ld_dst,
+                            int cap_rows, int pad_multiple, int32_t* dev_status, void* stream) {
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && width > 0 && cap_rows > 0 && pad_multiple > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d width=%d cap_rows=%d pad_multiple=%d)", n_tokens, block,
+          width, cap_rows, pad_multiple);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
+  lemo_status st;
+  if ((st = check_rows(src, ld_src, width, "src")) != LEMO_OK) return st;
+  if ((st = check_rows(dst, ld_dst, width, "dst")) != LEMO_OK) return st;
+  return device_status(lemo_launch_gather(src, n_tokens, width, ld_src, block, kept_blocks, n_kept, dst, ld_dst,
+                                          cap_rows, pad_multiple, dev_status, static_cast<hipStream_t>(stream)),
+                       "lemo_gather_pad launch");
+}
+
+lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                  const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y, int ld_y,
+                                  int32_t* dev_status, void* stream) {
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
+  lemo_status st;
+  if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
+  if ((st = check_rows(y, ld_y, width, "y")) != LEMO_OK) return st;
+  return device_status(lemo_launch_scatter(residual, n_tokens, width, ld_res, block, kept_blocks, n_kept, y, ld_y,
+                                           dev_status, static_cast<hipStream_t>(stream)),
+                       "lemo_scatter_residual launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the HIP translation units of liblemo.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lemo.h"
+
+typedef __bf16 lemo_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short lemo_i16x8 __attribute__((ext_vector_type(8)));
+typedef float lemo_f32x16 __attribute__((ext_vector_type(16)));
+typedef float lemo_f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 pattern -> fp32 value (exact).
+__device__ __forceinline__ float lemo_bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 pattern, round to nearest even.  Adding 0x7FFF plus the
+// lowest kept bit carries into the kept part exactly when the dropped half
+// is above the midpoint, or at it with an odd kept part; a carry out of the
+// significand moves to the next binade (and to infinity past the largest
+// finite value), as rounding requires.  NaN is kept a quiet NaN.
+__device__ __forceinline__ uint32_t lemo_f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Full-wave (64 lanes) maximum.
+__device__ __forceinline__ float lemo_wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Launchers (validated arguments only; return the hipError_t of the launch).
+hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_tokens, int n_heads,
+                                    int head_dim, int ld_q, int ld_k, int block, int head_reduce,
+                                    float* m_out, float* scores, hipStream_t stream);
+
+int lemo_predict_splitk(int nb, int d_model, int rank);
+size_t lemo_predict_ws_bytes(int n_tokens, int d_model, int block, int rank);
+hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int ld_x, int block,
+                               const uint16_t* u_q, const uint16_t* v_q, const uint16_t* u_k,
+                               const uint16_t* v_k, int rank, float* m_out, float* scores,
+                               void* workspace, hipStream_t stream);
+
+hipError_t lemo_launch_select(const float* scores, int n_blocks, int mode, float threshold,
+                              int keep_blocks, uint8_t* mask, int32_t* kept, int32_t* n_kept,
+                              float* threshold_used, int32_t* dev_status, hipStream_t stream);
+
+hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int ld_src, int block,
+                              const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst,
+                              int cap_rows, int pad_multiple, int32_t* dev_status, hipStream_t stream);
+
+hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block,
+                               const int32_t* kept, const int32_t* n_kept, const uint16_t* y, int ld_y,
+                               int32_t* dev_status, hipStream_t stream);
+
+hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream);
+
+static inline size_t lemo_align256(size_t x) { return (x + 255) & ~size_t(255); }

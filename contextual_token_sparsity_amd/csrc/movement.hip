@@ -1,0 +1,144 @@
+// Permutation-free token movement (Jenga, USENIX ATC'25, section 4.2.3):
+// "selective load" reads the kept tokens from their original rows, and
+// "in-place addition" adds the layer output of each kept token back into its
+// original row, so eliminated tokens are never copied, padded or touched.
+//
+// Both kernels are HBM-bound row copies: a workgroup of 256 threads moves a
+// 4 KiB column stripe (256 x 16 bytes) of a row per step, rows are strided
+// over the grid's y dimension, and each thread keeps four rows in flight.
+// The number of kept rows is read on the device (it comes from the select
+// step), so the grid is sized for the worst case and idle slots exit.
+#include "lemo_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b) {
+  const uint32_t* pa = &a.x;
+  const uint32_t* pb = &b.x;
+  uint4 o;
+  uint32_t* po = &o.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = lemo_bf16_to_f32(pa[j] & 0xffffu) + lemo_bf16_to_f32(pb[j] & 0xffffu);
+    const float hi = lemo_bf16_to_f32(pa[j] >> 16) + lemo_bf16_to_f32(pb[j] >> 16);
+    po[j] = lemo_f32_to_bf16(lo) | (lemo_f32_to_bf16(hi) << 16);
+  }
+  return o;
+}
+
+// Original token row of dense row p, or -1 when its kept index is invalid.
+__device__ __forceinline__ int token_of(const int32_t* __restrict__ kept, int p, int block, int nb) {
+  const int blk = kept[p / block];
+  return (blk >= 0 && blk < nb) ? blk * block + p % block : -1;
+}
+
+__global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict__ src, int n_tokens, int width,
+                                                     int ld_src, int block, const int32_t* __restrict__ kept,
+                                                     const int32_t* __restrict__ n_kept_p, uint16_t* __restrict__ dst,
+                                                     int ld_dst, int cap_rows, int pad_multiple,
+                                                     int32_t* __restrict__ status) {
+  const int nb = n_tokens / block;
+  const int nk = *n_kept_p;
+  const bool bad_count = nk < 0 || nk > nb;
+  const int n_rows = bad_count ? 0 : nk * block;
+  const long long n_pad = ((long long)n_rows + pad_multiple - 1) / pad_multiple * pad_multiple;
+  const int rows = (int)min((long long)cap_rows, n_pad);
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int flags = 0;
+    if (bad_count) flags |= LEMO_DEV_BAD_KEPT;
+    if (n_pad > cap_rows) flags |= LEMO_DEV_CAP_OVERFLOW;
+    if (flags) atomicOr(status, flags);
+  }
+  const int ch = blockIdx.x * kThreads + threadIdx.x;
+  if (ch * 8 >= width) return;
+  const int step = gridDim.y;
+  for (int p0 = blockIdx.y; p0 < rows; p0 += step * kUnroll) {
+    uint4 v[kUnroll];
+    int tok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + u * step;
+      v[u] = make_uint4(0, 0, 0, 0);
+      tok[u] = -1;
+      if (p < n_rows) {
+        tok[u] = token_of(kept, p, block, nb);
+        if (tok[u] >= 0) v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tok[u] * ld_src + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + u * step;
+      if (p >= rows) break;
+      if (p < n_rows && tok[u] < 0) {
+        if (status) atomicOr(status, LEMO_DEV_BAD_KEPT);
+        continue;
+      }
+      *reinterpret_cast<uint4*>(dst + (size_t)p * ld_dst + ch * 8) = v[u];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res, int n_tokens, int width, int ld_res,
+                                                      int block, const int32_t* __restrict__ kept,
+                                                      const int32_t* __restrict__ n_kept_p,
+                                                      const uint16_t* __restrict__ y, int ld_y,
+                                                      int32_t* __restrict__ status) {
+  const int nb = n_tokens / block;
+  const int nk = *n_kept_p;
+  const bool bad_count = nk < 0 || nk > nb;
+  const int n_rows = bad_count ? 0 : nk * block;
+  if (status && bad_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    atomicOr(status, LEMO_DEV_BAD_KEPT);
+  const int ch = blockIdx.x * kThreads + threadIdx.x;
+  if (ch * 8 >= width) return;
+  const int step = gridDim.y;
+  for (int p0 = blockIdx.y; p0 < n_rows; p0 += step * kUnroll) {
+    uint4 r[kUnroll], a[kUnroll];
+    int tok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int p = p0 + u * step;
+      tok[u] = p < n_rows ? token_of(kept, p, block, nb) : -2;
+      if (tok[u] >= 0) {
+        r[u] = *reinterpret_cast<const uint4*>(res + (size_t)tok[u] * ld_res + ch * 8);
+        a[u] = *reinterpret_cast<const uint4*>(y + (size_t)p * ld_y + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (tok[u] >= 0) {
+        *reinterpret_cast<uint4*>(res + (size_t)tok[u] * ld_res + ch * 8) = add_bf16x8(r[u], a[u]);
+      } else if (tok[u] == -1 && status) {
+        atomicOr(status, LEMO_DEV_BAD_KEPT);
+      }
+    }
+  }
+}
+
+dim3 grid_for(int width, int max_rows) {
+  const int gx = (width / 8 + kThreads - 1) / kThreads;
+  int gy = (2048 + gx - 1) / gx;
+  gy = max(1, min(gy, max_rows));
+  return dim3(gx, gy);
+}
+
+}  // namespace
+
+hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int ld_src, int block,
+                              const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst, int cap_rows,
+                              int pad_multiple, int32_t* dev_status, hipStream_t stream) {
+  hipLaunchKernelGGL(k_gather, grid_for(width, cap_rows), dim3(kThreads), 0, stream, src, n_tokens, width, ld_src,
+                     block, kept, n_kept, dst, ld_dst, cap_rows, pad_multiple, dev_status);
+  return hipGetLastError();
+}
+
+hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block, const int32_t* kept,
+                               const int32_t* n_kept, const uint16_t* y, int ld_y, int32_t* dev_status,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(k_scatter, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens, width, ld_res,
+                     block, kept, n_kept, y, ld_y, dev_status);
+  return hipGetLastError();
+}

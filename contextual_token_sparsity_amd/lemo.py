@@ -1,0 +1,196 @@
+"""Thin ctypes binding of liblemo.so (include/lemo.h), same names as the C ABI.
+
+Argument marshalling only: tensors are turned into device pointers, leading
+dimensions and the current HIP stream; every step of the hot path runs in the
+library's kernels.  There is no fallback: if the library is missing the first
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblemo.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "lemo.h")
+
+LEMO_OK = 0
+REDUCE_PAPER, REDUCE_HEADMAX = 0, 1
+SELECT_THRESHOLD, SELECT_TOPK, SELECT_MEAN = 0, 1, 2
+DEV_CAP_OVERFLOW, DEV_NONFINITE, DEV_BAD_KEPT = 1, 2, 4
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "lemo_block_scores_workspace": (_sz, [_i, _i]),
+    "lemo_block_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lemo_predict_scores_workspace": (_sz, [_i, _i, _i, _i]),
+    "lemo_predict_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lemo_select_mask": (_i, [_vp, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_status_string": (ctypes.c_char_p, [_i]),
+    "lemo_last_error": (ctypes.c_char_p, []),
+    "lemo_version": (_i, []),
+}
+
+_lib = None
+
+
+class LemoError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: status {status}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblemo.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m contextual_token_sparsity_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/lemo.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*\**\s+\**(lemo_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, fn: str):
+    if status != LEMO_OK:
+        raise LemoError(status, fn, lib().lemo_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a row-major 2-D tensor with unit column stride")
+    return t.stride(0)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _bf16(t):
+    if t.dtype not in (torch.int16, torch.uint16, torch.bfloat16):
+        raise TypeError("bf16 operands are passed as bfloat16 or 16-bit integer tensors")
+    if not t.is_cuda:
+        raise ValueError("operands must be device tensors")
+    return t
+
+
+# ---------------------------------------------------------------- calls
+def lemo_block_scores_workspace(n_tokens: int, block: int) -> int:
+    return lib().lemo_block_scores_workspace(n_tokens, block)
+
+
+def lemo_block_scores(q, k, n_heads: int, head_dim: int, block: int, head_reduce: int = REDUCE_PAPER,
+                      block_scores=None, scores=None, workspace=None):
+    """Exact block scores.  Returns (scores [nb] fp32, block_scores [nb][nb] or None)."""
+    _bf16(q), _bf16(k)
+    n = q.shape[0]
+    nb = n // block
+    if scores is None:
+        scores = torch.empty(nb, dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if block_scores is None:
+        ws_bytes = lemo_block_scores_workspace(n, block)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().lemo_block_scores(_ptr(q), _ptr(k), n, n_heads, head_dim, _ld(q), _ld(k), block, head_reduce,
+                                 _ptr(block_scores), _ptr(scores), _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0, _stream(q.device))
+    _check(st, "lemo_block_scores")
+    return scores, block_scores
+
+
+def lemo_predict_scores_workspace(n_tokens: int, d_model: int, block: int, rank: int) -> int:
+    return lib().lemo_predict_scores_workspace(n_tokens, d_model, block, rank)
+
+
+def lemo_predict_scores(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, block_scores=None,
+                        scores=None, workspace=None):
+    """Predicted block scores.  Returns (scores [nb] fp32, block_scores or None)."""
+    for t in (x, u_q, v_q, u_k, v_k):
+        _bf16(t)
+    n = x.shape[0]
+    d = x.shape[1] if d_model is None else d_model
+    rank = u_q.shape[1]
+    nb = n // block
+    if scores is None:
+        scores = torch.empty(nb, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(lemo_predict_scores_workspace(n, d, block, rank), 1), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().lemo_predict_scores(_ptr(x), n, d, _ld(x), block, _ptr(u_q), _ptr(v_q), _ptr(u_k), _ptr(v_k), rank,
+                                   _ptr(block_scores), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                   _stream(x.device))
+    _check(st, "lemo_predict_scores")
+    return scores, block_scores
+
+
+def lemo_select_mask(scores, mode: int, threshold: float = 0.0, keep_blocks: int = 0, mask=None, kept_blocks=None,
+                     n_kept=None, threshold_used=None, dev_status=None):
+    """Threshold + compaction.  Returns (mask u8, kept_blocks i32, n_kept i32[1], threshold_used f32[1])."""
+    nb = scores.shape[0]
+    dev = scores.device
+    mask = torch.empty(nb, dtype=torch.uint8, device=dev) if mask is None else mask
+    kept_blocks = torch.empty(nb, dtype=torch.int32, device=dev) if kept_blocks is None else kept_blocks
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    threshold_used = torch.empty(1, dtype=torch.float32, device=dev) if threshold_used is None else threshold_used
+    st = lib().lemo_select_mask(_ptr(scores), nb, mode, float(threshold), int(keep_blocks), _ptr(mask),
+                                _ptr(kept_blocks), _ptr(n_kept), _ptr(threshold_used), _ptr(dev_status),
+                                _stream(dev))
+    _check(st, "lemo_select_mask")
+    return mask, kept_blocks, n_kept, threshold_used
+
+
+def lemo_gather_pad(src, block: int, kept_blocks, n_kept, dst, pad_multiple: int = 1, width: int = None,
+                    n_tokens: int = None, dev_status=None):
+    """Selective load of the kept rows of src into dst (rows padded with zeros)."""
+    _bf16(src), _bf16(dst)
+    w = src.shape[1] if width is None else width
+    n = src.shape[0] if n_tokens is None else n_tokens
+    st = lib().lemo_gather_pad(_ptr(src), n, w, _ld(src), block, _ptr(kept_blocks), _ptr(n_kept), _ptr(dst),
+                               _ld(dst), dst.shape[0], pad_multiple, _ptr(dev_status), _stream(src.device))
+    _check(st, "lemo_gather_pad")
+    return dst
+
+
+def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: int = None, n_tokens: int = None,
+                          dev_status=None):
+    """In-place addition of y's rows into the kept rows of residual."""
+    _bf16(residual), _bf16(y)
+    w = residual.shape[1] if width is None else width
+    n = residual.shape[0] if n_tokens is None else n_tokens
+    st = lib().lemo_scatter_residual(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
+                                     _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
+    _check(st, "lemo_scatter_residual")
+    return residual
+
+
+def lemo_status_string(s: int) -> str:
+    return lib().lemo_status_string(s).decode()
+
+
+def lemo_last_error() -> str:
+    return lib().lemo_last_error().decode()
+
+
+def lemo_version() -> int:
+    return lib().lemo_version()

@@ -1,0 +1,200 @@
+/*
+ * lemo.h -- C ABI of the contextual-token-sparsity hot path on MI355X (gfx950).
+ *
+ * Per layer, the method decides which token blocks take part in the layer and
+ * moves only those rows:
+ *   exact block scores   lemo_block_scores      (pages: Eq. 1, Eq. 2, Figure 6)
+ *   predicted scores     lemo_predict_scores    (pages: Eq. 3, Figure 8)
+ *   threshold / compact  lemo_select_mask       (pages: layer threshold, Alg. 1 step 1)
+ *   selective load       lemo_gather_pad        (pages: permutation-free movement)
+ *   in-place addition    lemo_scatter_residual  (pages: permutation-free movement)
+ * "The pages" are "Jenga: Enhancing LLM Long-Context Fine-tuning with
+ * Contextual Token Sparsity" (USENIX ATC'25; summary page, section 4.2) and
+ * the review page of its arXiv version "LeMo" (2501.09767).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - bf16 values are passed as raw 16-bit patterns (lemo_bf16).  Matrices are
+ *    row-major; "ld" arguments are row strides in elements.
+ *  - Every pointer except the host-side scalars is DEVICE memory owned by the
+ *    caller.  The library allocates and frees nothing and keeps no per-call
+ *    state; scratch space comes from the caller through `workspace`, sized by
+ *    the matching *_workspace() query.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work; they never synchronise.  Outputs are valid once
+ *    the stream reaches them.  Device-resident results (n_kept, kept_blocks)
+ *    flow device-to-device between calls without a host round trip.
+ *  - Arguments are validated on the host BEFORE anything is enqueued: a
+ *    non-OK status means nothing was launched.  lemo_last_error() gives a
+ *    thread-local text for the last non-OK status.  A failing launch returns
+ *    LEMO_ERR_DEVICE.
+ *  - Device-side conditions never trap: kernels OR bits into the optional
+ *    int32 `dev_status` word (the caller clears it): LEMO_DEV_CAP_OVERFLOW,
+ *    LEMO_DEV_NONFINITE, LEMO_DEV_BAD_KEPT.
+ *  - Pointers to bf16 matrices must be 16-byte aligned and their ld a
+ *    multiple of 8 elements (128-bit row access).
+ *  - Inputs and outputs of one call must not overlap, except the residual of
+ *    lemo_scatter_residual, which is updated in place by design.
+ *  - Same inputs on the same device give bitwise-identical outputs (no
+ *    floating-point atomics anywhere).
+ *  - Calls are thread-safe; calls that share output buffers on one stream
+ *    are ordered by that stream.
+ */
+#ifndef LEMO_H
+#define LEMO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t lemo_bf16; /* raw bf16 bit pattern */
+
+typedef enum {
+  LEMO_OK = 0,
+  LEMO_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size, bad enum */
+  LEMO_ERR_UNSUPPORTED = 2,  /* valid but not implemented shape (block, head_dim, rank) */
+  LEMO_ERR_ALIGNMENT = 3,    /* pointer not 16-byte aligned or ld not a multiple of 8 */
+  LEMO_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query says */
+  LEMO_ERR_DEVICE = 5        /* a HIP call failed; see lemo_last_error() */
+} lemo_status;
+
+typedef enum {
+  /* Eq. 2 as printed: M[n][m] = max over (i in block n, j in block m, i != j)
+   * of (1/H) * sum_h max(0, S^h_ij) -- heads aggregated first, then block max. */
+  LEMO_REDUCE_PAPER = 0,
+  /* Per-head block max, clamped, then summed over heads:
+   * M[n][m] = sum_h max(0, max over (i in n, j in m, i != j) of S^h_ij). */
+  LEMO_REDUCE_HEADMAX = 1
+} lemo_head_reduce;
+
+typedef enum {
+  LEMO_SELECT_THRESHOLD = 0, /* keep block c iff I[c] >= threshold */
+  LEMO_SELECT_TOPK = 1,      /* keep the keep_blocks best blocks (ties: lower index) */
+  LEMO_SELECT_MEAN = 2       /* threshold = mean of I (Algorithm 1, step 1) */
+} lemo_select_mode;
+
+#define LEMO_DEV_CAP_OVERFLOW 1 /* gather: padded row count exceeded cap_rows; writes truncated */
+#define LEMO_DEV_NONFINITE 2    /* select: a NaN or infinite score was seen */
+#define LEMO_DEV_BAD_KEPT 4     /* gather/scatter: n_kept or a kept block index out of range; skipped */
+
+/* ------------------------------------------------------------------------
+ * Exact block scores (Jenga 4.2.1, Eq. 1 and Eq. 2; Figure 6 caption).
+ *
+ * For heads h < n_heads: S^h_ij = (Q^h_i . K^h_j) / sqrt(head_dim), the raw
+ * pre-softmax score (bf16 inputs, fp32 accumulation).  The N x N score matrix
+ * is cut into (block x block) tiles B^S_nm; each tile is reduced to one value
+ * M[n][m] as chosen by head_reduce (pairs i == j excluded), and the token
+ * block score is the column aggregate I[m] = sum over n of M[n][m].
+ * S never reaches memory: it lives in registers between the matrix-core
+ * product and the reduction.
+ *
+ *  q, k          bf16 [n_tokens][ld_q|ld_k]; head h occupies columns
+ *                h*head_dim .. h*head_dim+head_dim-1.
+ *  n_tokens      N > 0, a multiple of block.
+ *  head_dim      64 or 128.   block: 32, 64 or 128.
+ *  block_scores  optional fp32 [nb][nb] output M (row n = query block),
+ *                nb = n_tokens / block; NULL keeps M in the workspace.
+ *  scores        fp32 [nb] output I.
+ *  workspace     device scratch of lemo_block_scores_workspace() bytes when
+ *                block_scores is NULL; may be NULL / 0 bytes otherwise.
+ * Errors: INVALID_ARG (null q/k/scores, N % block, n_heads < 1,
+ * ld < n_heads*head_dim, bad head_reduce), UNSUPPORTED (head_dim, block),
+ * ALIGNMENT, WORKSPACE.  Non-finite inputs give unspecified scores.
+ * ------------------------------------------------------------------------ */
+size_t lemo_block_scores_workspace(int n_tokens, int block); /* bytes needed when block_scores is NULL */
+lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_tokens, int n_heads,
+                              int head_dim, int ld_q, int ld_k, int block, int head_reduce,
+                              float* block_scores, float* scores, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Predicted block scores (Jenga 4.2.2, Eq. 3 and Figure 8).
+ *
+ * Each token block's representative embedding is the mean of its rows,
+ *   xbar_m = bf16( (fp32 sum of the block's rows, in row order) / block );
+ * the query and key predictors are q_hat = bf16(ReLU(xbar U_q)) V_q and
+ * k_hat = bf16(ReLU(xbar U_k)) V_k (fp32 accumulation; q_hat, k_hat fp32);
+ * the block-pair score is M_hat[m][n] = max(0, q_hat_m . k_hat_n) and the
+ * token block score is the column aggregate I_hat[n] = sum over m of M_hat[m][n].
+ *
+ *  x             bf16 [n_tokens][ld_x] token embeddings, d_model columns used.
+ *  block         power of two, 2..256; n_tokens a multiple of it.
+ *  d_model       multiple of 64.   rank: multiple of 32, at most 256.
+ *  u_q, u_k      bf16 [d_model][rank] row-major.  v_q, v_k: bf16 [rank][rank].
+ *  block_scores  optional fp32 [nb][nb] M_hat (NULL: kept in workspace).
+ *  scores        fp32 [nb] I_hat.
+ *  workspace     lemo_predict_scores_workspace() bytes.
+ * Errors: INVALID_ARG, UNSUPPORTED (block, d_model, rank), ALIGNMENT, WORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int rank);
+lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layer threshold and compaction (Jenga 4.2.1, "Layer-specific Threshold";
+ * Algorithm 1 step 1 initialises the threshold to the average block score).
+ *
+ *  scores        fp32 [n_blocks] token block scores I (device).
+ *  n_blocks      1..8192.
+ *  mode          lemo_select_mode.  THRESHOLD uses `threshold`; MEAN computes
+ *                it as (float64 sum of I in block order) / n_blocks rounded to
+ *                fp32; TOPK keeps exactly keep_blocks blocks ordered by score
+ *                descending, ties to the lower index, NaN last.
+ *  mask          uint8 [n_blocks] out: 1 = keep.
+ *  kept_blocks   int32 [n_blocks] out: kept block indices, ascending, in the
+ *                first n_kept entries (the rest is left unchanged).
+ *  n_kept        int32 device scalar out.
+ *  threshold_used optional fp32 device scalar out (TOPK: the last kept score,
+ *                +inf when none is kept).
+ *  dev_status    optional; LEMO_DEV_NONFINITE is set when a score is NaN/inf.
+ * A block is kept iff score >= threshold (NaN never passes).
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_select_mask(const float* scores, int n_blocks, int mode, float threshold,
+                             int keep_blocks, uint8_t* mask, int32_t* kept_blocks, int32_t* n_kept,
+                             float* threshold_used, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Selective load (Jenga 4.2.3, Permutation-free Token Movement): the kept
+ * tokens are read from their original rows into a dense buffer.
+ *
+ *  dst[p] = src[kept_blocks[p / block] * block + p % block] for p < R,
+ *  R = n_kept * block (bit copy of `width` elements); rows R .. roundup(R,
+ *  pad_multiple)-1 are zeroed; rows beyond are not touched.  Rows at or past
+ *  cap_rows are never written (LEMO_DEV_CAP_OVERFLOW is set if R rounded up
+ *  exceeds cap_rows).  n_kept and kept_blocks are read on the device.
+ *  width         multiple of 8; ld_src, ld_dst >= width, multiples of 8.
+ *  cap_rows      rows of dst.   pad_multiple >= 1.
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int ld_src, int block,
+                            const int32_t* kept_blocks, const int32_t* n_kept, lemo_bf16* dst,
+                            int ld_dst, int cap_rows, int pad_multiple, int32_t* dev_status,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * In-place addition (Jenga 4.2.3): the layer output of every kept token is
+ * added to that token's original row of the residual stream; eliminated
+ * tokens are left bit-identical.
+ *
+ *  residual[t] = bf16_rne(fp32(residual[t]) + fp32(y[p])) for p < n_kept*block,
+ *  t = kept_blocks[p / block] * block + p % block, over `width` elements.
+ *  (fp32 add then round-to-nearest-even: the correctly rounded bf16 sum.)
+ *  y             bf16 [>= n_kept*block][ld_y], rows in kept order (as
+ *                lemo_gather_pad lays them out).
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                  const int32_t* kept_blocks, const int32_t* n_kept,
+                                  const lemo_bf16* y, int ld_y, int32_t* dev_status, void* stream);
+
+const char* lemo_status_string(lemo_status s);
+const char* lemo_last_error(void); /* thread-local detail of the last non-OK return */
+int lemo_version(void);            /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LEMO_H */

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (so these run without a GPU: the
+pointers below are never dereferenced)."""
+import ctypes
+
+import pytest
+
+from contextual_token_sparsity_amd import lemo
+
+OK, INVALID, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x100000)      # fake, 16-byte aligned, never touched
+P2 = ctypes.c_void_p(0x100002)     # misaligned
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lemo.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = lemo.declared_symbols()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert L.lemo_version() == 100
+    for s, text in ((0, "ok"), (1, "invalid argument"), (4, "workspace missing or too small")):
+        assert lemo.lemo_status_string(s) == text
+    assert lemo.lemo_status_string(99) == "unknown status"
+
+
+def test_workspace_queries(L):
+    assert L.lemo_block_scores_workspace(16384, 64) == 256 * 256 * 4
+    assert L.lemo_block_scores_workspace(100, 64) == 0
+    ws = L.lemo_predict_scores_workspace(16384, 4096, 64, 128)
+    # xbar (2 MiB) + split-K partials + q_hat/k_hat + M_hat
+    assert ws >= 256 * 4096 * 2 + 2 * 256 * 128 * 4 + 256 * 256 * 4
+    assert L.lemo_predict_scores_workspace(0, 4096, 64, 128) == 0
+
+
+def bs(L, q=P, k=P, n=1024, h=4, hd=128, ldq=512, ldk=512, b=64, mode=0, M=NULL, I=P, ws=NULL, wsb=0):
+    return L.lemo_block_scores(q, k, n, h, hd, ldq, ldk, b, mode, M, I, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=NULL), INVALID), (dict(q=NULL), INVALID), (dict(n=1000), INVALID), (dict(n=0), INVALID),
+    (dict(h=0), INVALID), (dict(mode=2), INVALID), (dict(ldq=256), INVALID),
+    (dict(hd=96, ldq=384, ldk=384), UNSUP), (dict(b=16), UNSUP), (dict(b=256), UNSUP),
+    (dict(mode=1, h=200, hd=64, ldq=12800, ldk=12800), UNSUP),
+    (dict(q=P2), ALIGN), (dict(ldk=516), ALIGN),
+    (dict(M=NULL, ws=NULL), WS), (dict(M=NULL, ws=P, wsb=100), WS),
+])
+def test_block_scores_rejects(L, kw, status):
+    assert bs(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def ps(L, x=P, n=1024, d=512, ldx=512, b=64, r=64, M=NULL, I=P, ws=P, wsb=1 << 30):
+    return L.lemo_predict_scores(x, n, d, ldx, b, P, P, P, P, r, M, I, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=NULL), INVALID), (dict(x=NULL), INVALID), (dict(n=1000), INVALID), (dict(r=0), INVALID),
+    (dict(ldx=256), INVALID), (dict(b=3, n=999), UNSUP), (dict(b=512, n=1024), UNSUP), (dict(b=1), UNSUP),
+    (dict(d=100, ldx=104), UNSUP), (dict(r=48), UNSUP), (dict(r=288), UNSUP),
+    (dict(x=P2), ALIGN), (dict(ldx=520 + 4), ALIGN),
+    (dict(ws=NULL), WS), (dict(wsb=1000), WS),
+])
+def test_predict_rejects(L, kw, status):
+    assert ps(L, **kw) == status
+
+
+def sel(L, s=P, nb=256, mode=1, th=0.0, k=10, mask=P, kept=P, nk=P):
+    return L.lemo_select_mask(s, nb, mode, th, k, mask, kept, nk, NULL, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(s=NULL), INVALID), (dict(mask=NULL), INVALID), (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID),
+    (dict(nb=0), INVALID), (dict(nb=8193), UNSUP), (dict(mode=3), INVALID), (dict(k=257), INVALID),
+    (dict(k=-1), INVALID),
+])
+def test_select_rejects(L, kw, status):
+    assert sel(L, **kw) == status
+
+
+def ga(L, src=P, n=1024, w=512, lds=512, b=64, kept=P, nk=P, dst=P, ldd=512, cap=1024, pad=256):
+    return L.lemo_gather_pad(src, n, w, lds, b, kept, nk, dst, ldd, cap, pad, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID), (dict(src=NULL), INVALID), (dict(dst=NULL), INVALID),
+    (dict(n=1000), INVALID), (dict(cap=0), INVALID), (dict(pad=0), INVALID), (dict(ldd=256), INVALID),
+    (dict(w=12, lds=16, ldd=16), ALIGN), (dict(dst=P2), ALIGN), (dict(lds=520 + 2), ALIGN),
+])
+def test_gather_rejects(L, kw, status):
+    assert ga(L, **kw) == status
+
+
+def sc(L, res=P, n=1024, w=512, ldr=512, b=64, kept=P, nk=P, y=P, ldy=512):
+    return L.lemo_scatter_residual(res, n, w, ldr, b, kept, nk, y, ldy, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(res=NULL), INVALID), (dict(y=NULL), INVALID), (dict(n=1000), INVALID),
+    (dict(b=0), INVALID), (dict(ldy=256), INVALID), (dict(w=4, ldr=8, ldy=8), ALIGN), (dict(y=P2), ALIGN),
+])
+def test_scatter_rejects(L, kw, status):
+    assert sc(L, **kw) == status

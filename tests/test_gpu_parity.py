@@ -1,0 +1,435 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs (and never on inputs produced by the HIP path).
+
+Bars: scores within relative 1e-2 (floor 1e-6 of the largest score); masks
+equal except on blocks whose oracle score is within 1e-2 of the oracle
+threshold; select, gather and scatter bit-exact given the same inputs.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from contextual_token_sparsity_amd import lemo
+from contextual_token_sparsity_amd import synth
+from oracle import lemo_oracle as O
+from tests.gpu_helpers import dev, host_bits, mask_acceptable, padded, scores_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lemo.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rand_qk(seed, n, h, hd, std=1.0):
+    rng = np.random.default_rng(seed)
+    return synth.random_bf16(rng, (n, h * hd), std), synth.random_bf16(rng, (n, h * hd), std)
+
+
+# ----------------------------------------------------------- exact scores
+EXACT_SMALL = [
+    # (N, H, hd, block)
+    (256, 2, 128, 64),
+    (320, 3, 64, 64),     # N not a multiple of the 128-row tile: ragged last tile
+    (224, 2, 128, 32),    # ragged, 32-row blocks (one block per MFMA tile)
+    (384, 2, 64, 128),    # 128-row blocks span the four waves of a tile
+    (96, 1, 64, 32),      # smaller than one tile
+    (64, 1, 128, 64),     # a single block: only diagonal pairs to exclude
+    (1024, 5, 128, 64),
+]
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+@pytest.mark.parametrize("shape", EXACT_SMALL, ids=lambda s: "N%d_H%d_hd%d_b%d" % s)
+def test_exact_small(shape, mode):
+    n, h, hd, b = shape
+    say("exact", shape, mode)
+    q, k = rand_qk(1000 + n + h, n, h, hd)
+    M_ref, I_ref = O.exact_block_scores(q, k, h, hd, b, mode)
+    nb = n // b
+    M = torch.full((nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_block_scores(dev(q), dev(k), h, hd, b, mode, block_scores=M)
+    torch.cuda.synchronize()
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok, worst
+    okm, worstm = scores_close(M.cpu().numpy(), M_ref)
+    assert okm, worstm
+    assert worst < 1e-4 and worstm < 1e-4, (worst, worstm)   # fp32 accumulation, not 1e-2
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+@pytest.mark.parametrize("wname", ["tiny", "opt1.3b-n4k"])
+def test_exact_workload(wname, mode):
+    w = synth.WORKLOADS[wname]
+    say("exact workload", wname, mode)
+    L = synth.make_workload(w, with_y=False)
+    M_ref, I_ref = O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, mode)
+    I, _ = lemo.lemo_block_scores(dev(L.q), dev(L.k), w.n_heads, w.head_dim, w.block, mode)
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok and worst < 1e-4, worst
+
+
+def _sampled_check(q, k, h, hd, b, mode, entries, columns, M_gpu, I_gpu):
+    for (r, c) in entries:
+        M_ref, _ = O.exact_block_scores(q, k, h, hd, b, mode, query_blocks=[r], key_blocks=[c])
+        ok, worst = scores_close([M_gpu[r, c]], M_ref[0])
+        assert ok and worst < 1e-4, (r, c, M_gpu[r, c], M_ref[0, 0])
+    for c in columns:
+        I_ref, col = O.exact_column_score(q, k, h, hd, b, mode, c)
+        ok, worst = scores_close(M_gpu[:, c], col)
+        assert ok, (c, worst)
+        ok, worst = scores_close([I_gpu[c]], [I_ref])
+        assert ok and worst < 1e-4, (c, I_gpu[c], I_ref)
+
+
+@pytest.mark.parametrize("wname", ["llama2-7b-n8k-exact", "llama2-7b-n16k"])
+def test_exact_full_size_sampled(wname):
+    """Full-size exact scoring in the benchmark's launch configuration; the
+    oracle recomputes sampled block scores and whole columns one by one."""
+    w = synth.WORKLOADS[wname]
+    say("exact full size", wname)
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, n_heads=w.n_heads, head_dim=w.head_dim,
+                         planted_frac=w.planted_frac, with_y=False, proj_device="cuda")
+    nb = w.n_blocks
+    rng = np.random.default_rng(5)
+    entries = [(0, 0), (nb - 1, nb - 1), (nb // 2, nb // 2)] + [tuple(rng.integers(0, nb, 2)) for _ in range(5)]
+    columns = [int(L.planted_blocks[0]) if L.planted_blocks.size else 1, nb - 1]
+    qd, kd = dev(L.q), dev(L.k)
+    for mode in (O.REDUCE_PAPER, O.REDUCE_HEADMAX):
+        M = torch.empty((nb, nb), device="cuda")
+        I, _ = lemo.lemo_block_scores(qd, kd, w.n_heads, w.head_dim, w.block, mode, block_scores=M)
+        _sampled_check(L.q, L.k, w.n_heads, w.head_dim, w.block, mode, entries, columns,
+                       M.cpu().numpy(), I.cpu().numpy())
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+def test_exact_closed_form_full_size(mode):
+    """Q_i = a e and K_j = beta_j e in every head (e one coordinate): every
+    block score of key block m is a max_{j in m} beta_j / sqrt(hd), times H
+    for HEADMAX, so I[m] is nb times that -- at N = 16384, no oracle needed."""
+    n, h, hd, b = 16384, 32, 128, 64
+    nb = n // b
+    rng = np.random.default_rng(21)
+    a = 0.75
+    beta = synth.to_bf16_bits(np.abs(rng.standard_normal(n)).astype(np.float32))
+    bf = synth.bf16_bits_to_f32(beta).astype(np.float64)
+    q = np.zeros((n, h * hd), np.uint16)
+    k = np.zeros((n, h * hd), np.uint16)
+    q[:, 3::hd] = synth.to_bf16_bits(np.full((1,), a, np.float32))[0]
+    k[:, 3::hd] = beta[:, None]
+    I, _ = lemo.lemo_block_scores(dev(q), dev(k), h, hd, b, mode)
+    expect = nb * a * bf.reshape(nb, b).max(axis=1) / math.sqrt(hd) * (h if mode == O.REDUCE_HEADMAX else 1)
+    ok, worst = scores_close(I.cpu().numpy(), expect, rel=1e-5)
+    assert ok, worst
+
+
+def test_exact_deterministic():
+    q, k = rand_qk(77, 1024, 4, 128)
+    outs = []
+    for _ in range(2):
+        M = torch.empty((16, 16), device="cuda")
+        I, _ = lemo.lemo_block_scores(dev(q), dev(k), 4, 128, 64, O.REDUCE_PAPER, block_scores=M)
+        outs.append((I.cpu().numpy().tobytes(), M.cpu().numpy().tobytes()))
+    assert outs[0] == outs[1]
+
+
+def test_exact_strided_operands():
+    """Q and K read from wider rows (ld > H*hd), e.g. slices of a fused QKV."""
+    n, h, hd, b = 256, 2, 64, 64
+    q, k = rand_qk(9, n, h, hd)
+    _, I_ref = O.exact_block_scores(q, k, h, hd, b, O.REDUCE_PAPER)
+    qp, kp = padded(q, 200, 0x7FC0), padded(k, 136, 0x7FC0)   # NaN in the unused columns
+    I, _ = lemo.lemo_block_scores(qp[:, :h * hd], kp[:, :h * hd], h, hd, b, O.REDUCE_PAPER)
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok and worst < 1e-4
+
+
+# ------------------------------------------------------------- predictor
+PRED_SMALL = [
+    # (N, d, block, rank)
+    (256, 128, 4, 32),
+    (512, 256, 2, 64),
+    (1024, 512, 64, 32),
+    (2048, 192, 8, 96),
+    (4096, 320, 256, 256),
+]
+
+
+def _pred_inputs(seed, n, d, r, planted=0.2, b=64):
+    rng = np.random.default_rng(seed)
+    x = synth.random_bf16(rng, (n, d))
+    w = [synth.random_bf16(rng, s, 1.0 / math.sqrt(s[0])) for s in ((d, r), (r, r), (d, r), (r, r))]
+    return x, w
+
+
+def _check_pred(x, w, b, d_model=None, xdev=None):
+    n = x.shape[0]
+    nb = n // b
+    M_ref, I_ref, _, _ = O.predict_scores(x, *w, b)
+    M = torch.full((nb, nb), -1.0, device="cuda")
+    xd = dev(x) if xdev is None else xdev
+    I, _ = lemo.lemo_predict_scores(xd, *[dev(a) for a in w], b, d_model=d_model, block_scores=M)
+    Ig, Mg = I.cpu().numpy(), M.cpu().numpy()
+    ok, worst = scores_close(Ig, I_ref)
+    assert ok, worst
+    merr = np.abs(Mg - M_ref) <= 1e-2 * np.abs(M_ref) + 1e-3 * np.abs(M_ref).max()
+    assert merr.all(), float(np.abs(Mg - M_ref).max())
+    return worst
+
+
+@pytest.mark.parametrize("shape", PRED_SMALL, ids=lambda s: "N%d_d%d_b%d_r%d" % s)
+def test_predict_small(shape):
+    n, d, b, r = shape
+    say("predict", shape)
+    x, w = _pred_inputs(n + d + r, n, d, r)
+    worst = _check_pred(x, w, b)
+    assert worst < 1e-3, worst
+
+
+@pytest.mark.parametrize("wname", ["llama2-7b-n16k", "llama2-13b-n32k-4layer"])
+def test_predict_workload(wname):
+    w = synth.WORKLOADS[wname]
+    say("predict workload", wname)
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, rank=w.rank, planted_frac=w.planted_frac,
+                         with_y=False)
+    worst = _check_pred(L.x, [L.u_q, L.v_q, L.u_k, L.v_k], w.block)
+    assert worst < 1e-3, worst
+
+
+def test_predict_strided_x():
+    n, d, b, r = 512, 128, 8, 32
+    x, w = _pred_inputs(3, n, d, r)
+    xp = padded(x, 200 + 0, 0x7FC0)
+    _check_pred(x, w, b, xdev=xp[:, :d])
+
+
+# ---------------------------------------------------------------- select
+def _select_case(scores_f32, mode, threshold=0.0, keep=0):
+    s = np.asarray(scores_f32, np.float32)
+    nb = s.size
+    mask_r, kept_r, nk_r, th_r = O.select_mask(s, mode, threshold, keep)
+    kept = torch.full((nb,), -7, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mask, kept, nk, th = lemo.lemo_select_mask(dev(s), mode, threshold, keep, kept_blocks=kept, dev_status=status)
+    nk = int(nk.item())
+    kept = kept.cpu().numpy()
+    assert nk == nk_r
+    assert np.array_equal(mask.cpu().numpy(), mask_r)
+    assert np.array_equal(kept[:nk], kept_r)
+    assert np.all(kept[nk:] == -7)
+    thg = th.cpu().numpy()[0]
+    assert (np.isnan(thg) and np.isnan(th_r)) or thg.tobytes() == np.float32(th_r).tobytes(), (thg, th_r)
+    st = int(status.item())
+    assert bool(st & lemo.DEV_NONFINITE) == (not np.isfinite(s).all())
+
+
+@pytest.mark.parametrize("nb", [1, 5, 64, 256, 1000, 1025, 4097, 8192])
+@pytest.mark.parametrize("mode", ["threshold", "mean", "topk"])
+def test_select_random(nb, mode):
+    rng = np.random.default_rng(nb)
+    s = (rng.random(nb) * 10).astype(np.float32)
+    if mode == "threshold":
+        _select_case(s, O.SELECT_THRESHOLD, threshold=float(np.median(s)))
+    elif mode == "mean":
+        _select_case(s, O.SELECT_MEAN)
+    else:
+        for k in sorted({0, 1, nb // 3, nb - 1, nb} - {-1}):
+            if 0 <= k <= nb:
+                _select_case(s, O.SELECT_TOPK, keep=k)
+
+
+def test_select_edge_values():
+    ties = np.array([3, 1, 3, 3, 2, 3, 0, 3], np.float32)
+    for k in range(9):
+        _select_case(ties, O.SELECT_TOPK, keep=k)
+    _select_case(ties, O.SELECT_THRESHOLD, threshold=3.0)
+    _select_case(ties, O.SELECT_MEAN)
+    zeros = np.array([0.0, -0.0, 0.0, 1.0, -0.0], np.float32)
+    for k in range(6):
+        _select_case(zeros, O.SELECT_TOPK, keep=k)
+    _select_case(zeros, O.SELECT_THRESHOLD, threshold=-0.0)
+    nan = np.array([np.nan, 2, np.inf, 1, np.nan, -np.inf], np.float32)
+    for k in range(7):
+        _select_case(nan, O.SELECT_TOPK, keep=k)
+    _select_case(nan, O.SELECT_THRESHOLD, threshold=1.5)
+    _select_case(nan, O.SELECT_MEAN)
+    same = np.full(300, 0.25, np.float32)
+    _select_case(same, O.SELECT_TOPK, keep=77)
+    _select_case(same, O.SELECT_MEAN)
+
+
+def test_select_on_oracle_scores():
+    """The realistic case: scores of a real workload (oracle's, rounded to fp32)."""
+    w = synth.WORKLOADS["tiny"]
+    L = synth.make_workload(w, with_y=False)
+    _, I_ref = O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER)
+    s = I_ref.astype(np.float32)
+    _select_case(s, O.SELECT_MEAN)
+    _select_case(s, O.SELECT_TOPK, keep=synth.keep_count(50, w.n_blocks))
+
+
+# ------------------------------------------------------- gather / scatter
+MOVE = [
+    # (N, width, ld_src, ld_dst, block, keep fraction, pad_multiple, cap extra rows)
+    (256, 64, 64, 64, 4, 0.5, 1, 0),
+    (1024, 512, 520, 512, 64, 0.5, 256, 8),
+    (2048, 8, 16, 8, 16, 0.3, 7, 3),
+    (4096, 2048, 2048, 2056, 64, 0.4, 256, 0),
+    (1024, 1376, 1376, 1376, 32, 1.0, 64, 0),     # keep all
+    (1024, 256, 256, 256, 64, 0.0, 256, 5),       # keep none
+    (16384, 11008, 11008, 11008, 64, 0.35, 256, 0),  # MLP activation width
+]
+
+
+def _kept_from_mask(rng, nb, frac):
+    m = rng.random(nb) < frac
+    if frac >= 1.0:
+        m[:] = True
+    return np.nonzero(m)[0].astype(np.int32)
+
+
+@pytest.mark.parametrize("case", MOVE, ids=lambda c: "N%d_w%d_b%d_keep%.2f_pad%d" % (c[0], c[1], c[4], c[5], c[6]))
+def test_gather_scatter(case):
+    n, w, lds, ldd, b, frac, pad, extra = case
+    say("move", case)
+    rng = np.random.default_rng(n + w)
+    nb = n // b
+    kept = _kept_from_mask(rng, nb, frac)
+    nk = kept.size
+    src = synth.random_bf16(rng, (n, w))
+    R = nk * b
+    cap = max(1, -(-R // pad) * pad + extra)
+    sentinel = np.full((cap, w), 0x5A5A, np.uint16)
+    dst_ref, over_ref = O.gather_pad(src, b, kept, nk, sentinel, pad)
+    kept_d = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    kept_d[:nk] = torch.from_numpy(kept).cuda()
+    nk_d = torch.tensor([nk], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    srcd = padded(src, lds, 0x7FC0)
+    dstd = padded(sentinel, ldd, 0x1234)
+    lemo.lemo_gather_pad(srcd[:, :w], b, kept_d, nk_d, dstd[:, :w], pad_multiple=pad, dev_status=status)
+    got = host_bits(dstd)
+    assert np.array_equal(got[:, :w], dst_ref)
+    assert np.all(got[:, w:] == 0x1234)
+    assert int(status.item()) == 0 and not over_ref
+    # scatter: y rows in kept order, residual updated in place
+    res = synth.random_bf16(rng, (n, w))
+    y = synth.random_bf16(rng, (max(R, 1), w))
+    res_ref = O.scatter_residual(res, b, kept, nk, y)
+    resd = padded(res, lds, 0x4321)
+    yd = padded(y, ldd, 0x7FC0)
+    lemo.lemo_scatter_residual(resd[:, :w], b, kept_d, nk_d, yd[:, :w], dev_status=status)
+    got = host_bits(resd)
+    assert np.array_equal(got[:, :w], res_ref)
+    assert np.all(got[:, w:] == 0x4321)
+    assert int(status.item()) == 0
+
+
+def test_gather_capacity_overflow():
+    n, w, b = 512, 64, 16
+    rng = np.random.default_rng(2)
+    kept = np.arange(0, 32, 2, dtype=np.int32)          # 16 blocks = 256 rows
+    src = synth.random_bf16(rng, (n, w))
+    cap = 200                                            # < 256 rows, pad 64 -> 256
+    dst_ref, over = O.gather_pad(src, b, kept, kept.size, np.full((cap, w), 0x5A5A, np.uint16), 64)
+    assert over
+    dstd = dev(np.full((cap, w), 0x5A5A, np.uint16))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lemo.lemo_gather_pad(dev(src), b, dev(kept), dev(np.array([kept.size], np.int32)), dstd, pad_multiple=64,
+                         dev_status=status)
+    assert np.array_equal(host_bits(dstd), dst_ref)
+    assert int(status.item()) & lemo.DEV_CAP_OVERFLOW
+
+
+def test_bad_kept_indices_are_skipped_and_flagged():
+    n, w, b = 256, 32, 8
+    nb = n // b
+    rng = np.random.default_rng(4)
+    src = synth.random_bf16(rng, (n, w))
+    kept = np.array([1, 40, 3, -2], np.int32)            # 40 and -2 are out of range
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dstd = dev(np.full((32, w), 0x5A5A, np.uint16))
+    lemo.lemo_gather_pad(dev(src), b, dev(kept), dev(np.array([4], np.int32)), dstd, dev_status=status)
+    got = host_bits(dstd)
+    assert np.array_equal(got[0:8], src[8:16]) and np.array_equal(got[16:24], src[24:32])
+    assert np.all(got[8:16] == 0x5A5A) and np.all(got[24:32] == 0x5A5A)
+    assert int(status.item()) & lemo.DEV_BAD_KEPT
+    status.zero_()
+    res = synth.random_bf16(rng, (n, w))
+    resd = dev(res)
+    lemo.lemo_scatter_residual(resd, b, dev(kept), dev(np.array([nb + 1], np.int32)), dev(src), dev_status=status)
+    assert np.array_equal(host_bits(resd), res) and int(status.item()) & lemo.DEV_BAD_KEPT
+
+
+def test_movement_full_size_oracle_mask():
+    """The benchmark's Llama2-7B N=16K movement with the oracle's predicted
+    mask (MEAN threshold): gather of X and of the MLP activation padded to
+    256 rows, then the in-place residual add, all bit-exact."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("movement full size")
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, rank=w.rank, mlp_width=w.mlp_width,
+                         planted_frac=w.planted_frac)
+    _, I_ref, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
+    _, kept, nk, _ = O.select_mask(I_ref.astype(np.float32), O.SELECT_MEAN)
+    R = nk * w.block
+    cap = -(-R // 256) * 256
+    kd, nkd = dev(kept), dev(np.array([nk], np.int32))
+    xd = dev(L.x)
+    for src, width in ((L.x, w.d_model), (L.act, w.mlp_width)):
+        ref, _ = O.gather_pad(src, w.block, kept, nk, np.zeros((cap, width), np.uint16), 256)
+        dstd = torch.empty((cap, width), dtype=torch.int16, device="cuda")
+        lemo.lemo_gather_pad(xd if src is L.x else dev(src), w.block, kd, nkd, dstd, pad_multiple=256)
+        assert np.array_equal(host_bits(dstd), ref)
+    rows = O.kept_token_rows(kept, nk, w.block)
+    y = L.y[rows]
+    res_ref = O.scatter_residual(L.x, w.block, kept, nk, y)
+    lemo.lemo_scatter_residual(xd, w.block, kd, nkd, dev(y))
+    assert np.array_equal(host_bits(xd), res_ref)
+
+
+# -------------------------------------------------------------- pipeline
+@pytest.mark.parametrize("path", ["exact", "predictor"])
+def test_pipeline_tiny(path):
+    """Scores -> select (top-k 50%) -> gather -> scatter on the GPU, chained
+    on one stream with no host round trip, against the oracle's own chain."""
+    w = synth.WORKLOADS["tiny"]
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, n_heads=w.n_heads, head_dim=w.head_dim, rank=64,
+                         planted_frac=w.planted_frac)
+    k = synth.keep_count(50, w.n_blocks)
+    if path == "exact":
+        _, I_ref = O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER)
+        I, _ = lemo.lemo_block_scores(dev(L.q), dev(L.k), w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER)
+    else:
+        _, I_ref, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
+        I, _ = lemo.lemo_predict_scores(dev(L.x), dev(L.u_q), dev(L.v_q), dev(L.u_k), dev(L.v_k), w.block)
+    mask_r, kept_r, nk_r, th_r = O.select_mask(I_ref.astype(np.float32), O.SELECT_TOPK, keep_blocks=k)
+    mask, kept, nk, th = lemo.lemo_select_mask(I, O.SELECT_TOPK, keep_blocks=k)
+    xd = dev(L.x)
+    cap = w.n_tokens
+    dst = torch.zeros((cap, w.d_model), dtype=torch.int16, device="cuda")
+    lemo.lemo_gather_pad(xd, w.block, kept, nk, dst, pad_multiple=256)
+    y_full = dev(L.y)
+    # the stand-in layer output of dense row p is Y_full[token(p)]: gather it too
+    yk = torch.zeros((cap, w.d_model), dtype=torch.int16, device="cuda")
+    lemo.lemo_gather_pad(y_full, w.block, kept, nk, yk)
+    lemo.lemo_scatter_residual(xd, w.block, kept, nk, yk)
+    torch.cuda.synchronize()
+    ok, diff = mask_acceptable(mask.cpu().numpy(), mask_r, I_ref, th_r)
+    assert ok, diff
+    if diff.size == 0:
+        ref_dst, _ = O.gather_pad(L.x, w.block, kept_r, nk_r, np.zeros((cap, w.d_model), np.uint16), 256)
+        assert np.array_equal(host_bits(dst), ref_dst)
+        rows = O.kept_token_rows(kept_r, nk_r, w.block)
+        ref_res = O.scatter_residual(L.x, w.block, kept_r, nk_r, L.y[rows])
+        assert np.array_equal(host_bits(xd), ref_res)
