@@ -5,86 +5,98 @@
 // (block x block) score tile is reduced to one value M[n][m] and the token
 // block score is I[m] = sum_n M[n][m].  Pairs i == j are excluded.
 //
-// Work decomposition: one workgroup owns a 128 x 128 tile of (query rows,
-// key rows) and walks all heads.  Per head the Q and K head slices of the
-// tile are staged in LDS and four waves each multiply a 64 x 64 sub-tile with
-// v_mfma_f32_32x32x16_bf16 (2 x 2 MFMA tiles, fp32 accumulators).  The score
-// tile never leaves registers:
-//   PAPER   (heads first, then block max): the running sum over heads of
-//           max(0, S^h) is kept per element.  Each head's MFMA chain starts
-//           from that running sum as its C operand, so after the chain
-//           acc = sum + S^h and the update sum = max(acc, sum) costs one VALU
-//           op per element and head.
-//   HEADMAX (per-head block max): after each head the wave reduces its
-//           accumulators to the block maximum of that head; the per-head
-//           maxima are clamped at zero and summed after the head loop.
-// The i == j pairs sit on the diagonal of diagonal tiles; they are set to 0,
-// which leaves both reductions unchanged (PAPER values are >= 0 and HEADMAX
-// clamps at 0 after the max).  The scale 1/sqrt(head_dim) (and 1/H for
-// PAPER) is applied once to the block value, which is exact up to rounding
-// because every step is positively homogeneous.
+// Work decomposition
+//   One workgroup (8 waves) owns a 256 x 128 tile of (query rows, key rows)
+//   and walks every head.  Each wave multiplies a 64 x 64 sub-tile with
+//   v_mfma_f32_32x32x16_bf16 (2 x 2 MFMA tiles, fp32 accumulators in VGPRs).
+//   The head dimension is streamed in 64-wide chunks through a 3-stage LDS
+//   ring filled by direct global->LDS loads (global_load_lds_dwordx4), so the
+//   loads of chunk c+2 are in flight while chunk c multiplies; one barrier per
+//   chunk.  LDS rows are 128 B; the 16-B pieces of row r are stored XOR-
+//   swizzled (piece p at p ^ swz(r)) so that the MFMA operand reads (32 rows,
+//   one piece each) hit distinct banks.
+//
+// The score tile never leaves registers:
+//   PAPER   (heads first, then block max): each head's MFMA chain starts from
+//           the running sum over heads of max(0, S^h) as its C operand, so
+//           after the chain acc = sum + S^h, and sum = max(acc, sum) is the
+//           update.  sum >= 0 always, and for a non-negative float the bit
+//           pattern orders like a signed integer while a negative float is a
+//           negative integer: the update is one v_max_i32 per element.
+//   HEADMAX (per-head block max): the head's accumulators are reduced with
+//           v_max_i32 starting from 0, which yields max(0, block max) (the
+//           clamp is free for the same reason), then across lanes; the clamped
+//           per-head maxima are summed over heads in head order.
+// The i == j pairs sit on the diagonal of diagonal sub-tiles; they are set to
+// 0, which changes neither reduction (PAPER values are >= 0, HEADMAX clamps at
+// 0).  The scale 1/sqrt(head_dim) (and 1/H for PAPER) is applied once to the
+// block value; every step is positively homogeneous so this is exact up to
+// rounding.
 //
 // The column aggregate is a second, deterministic pass (k_colsum).
+#include <type_traits>
+
 #include "lemo_internal.h"
 
 namespace {
 
-constexpr int kTile = 128;     // query rows x key rows per workgroup
-constexpr int kThreads = 256;  // 4 waves, 2 x 2 arrangement of 64 x 64
+constexpr int kTQ = 256;        // query rows per workgroup
+constexpr int kTK = 128;        // key rows per workgroup
+constexpr int kWaves = 8;       // 4 (query) x 2 (key) waves of 64 x 64
+constexpr int kThreads = kWaves * 64;
+constexpr int kChunk = 64;      // head-dim elements per pipeline stage
+constexpr int kRowBytes = kChunk * 2;
+constexpr int kStageQ = kTQ * kRowBytes;           // 32 KiB
+constexpr int kStageK = kTK * kRowBytes;           // 16 KiB
+constexpr int kStageBytes = kStageQ + kStageK;     // 48 KiB
+constexpr int kStages = 3;
+constexpr int kDmaQ = kStageQ / (kThreads * 16);   // 4 loads of 16 B per thread
+constexpr int kDmaK = kStageK / (kThreads * 16);   // 2
+constexpr int kDmaPerChunk = kDmaQ + kDmaK;
 constexpr int kMaxHeadsHeadmax = 128;
 
-template <int HD>
-struct Cfg {
-  static constexpr int kRow = HD + 8;          // LDS row pitch (bf16): +16 B breaks bank aliasing
-  static constexpr int kChunks = HD / 8;       // 16-byte chunks per row slice
-  static constexpr int kPerThread = kTile * kChunks / kThreads;
-};
+static_assert(kDmaQ * kThreads * 16 == kStageQ && kDmaK * kThreads * 16 == kStageK, "stage split");
 
-// Output (row, col) of register `r` of `lane` in a 32x32 MFMA accumulator.
-__device__ __forceinline__ int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage[kStages * kStageBytes];
 
-template <int HD>
-__device__ __forceinline__ void load_head(const uint16_t* __restrict__ base, int ld, int row0, int n_tokens,
-                                          int col0, uint4 (&v)[Cfg<HD>::kPerThread]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < Cfg<HD>::kPerThread; ++i) {
-    const int c = tid + i * kThreads;
-    const int r = c / Cfg<HD>::kChunks;
-    const int cc = c % Cfg<HD>::kChunks;
-    if (row0 + r < n_tokens)
-      v[i] = *reinterpret_cast<const uint4*>(base + (size_t)(row0 + r) * ld + col0 + cc * 8);
-    else
-      v[i] = make_uint4(0, 0, 0, 0);
-  }
+// Piece swizzle of LDS row r: distinct for 8 consecutive rows and for the 8
+// even (odd) rows among 16 consecutive rows, so a wave's 32-row operand read
+// is conflict-free whether the LDS serves 8 or 16 pieces per cycle.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// Output row of register e of `lane` in a 32x32 MFMA accumulator (column = lane % 32).
+__device__ __forceinline__ int acc_row(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// One 16-byte direct global->LDS load per lane: lane l reads base + voff and
+// writes lds_base + 16 l.  (No register result; completion is tracked with
+// vmcnt by the caller.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(base) : "memory");
 }
 
-template <int HD>
-__device__ __forceinline__ void store_head(uint16_t* s, const uint4 (&v)[Cfg<HD>::kPerThread]) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+__device__ __forceinline__ int wave_imax(int v) {
 #pragma unroll
-  for (int i = 0; i < Cfg<HD>::kPerThread; ++i) {
-    const int c = tid + i * kThreads;
-    const int r = c / Cfg<HD>::kChunks;
-    const int cc = c % Cfg<HD>::kChunks;
-    *reinterpret_cast<uint4*>(s + r * Cfg<HD>::kRow + cc * 8) = v[i];
-  }
+  for (int off = 32; off >= 1; off >>= 1) v = imax(v, __shfl_xor(v, off, 64));
+  return v;
 }
 
-// Maps a linear workgroup id to a (query tile, key tile) pair.  Consecutive
-// dispatches go round-robin over the 8 XCDs; this gives each XCD a
-// contiguous range of logical tiles, walked in groups of 8 query tiles, so
-// that the workgroups resident on one XCD share Q and K rows in its L2.
-__device__ __forceinline__ void tile_of(int wg, int ntiles, int& tq, int& tk) {
-  const int total = ntiles * ntiles;
+// Maps a linear workgroup id to a (query tile, key tile) pair.  Dispatch goes
+// round-robin over the 8 XCDs; each XCD gets a contiguous range of logical
+// tiles, walked in groups of 4 query tiles so that the ~32 workgroups
+// resident on one XCD cover a 4 x 8 patch of tiles and share Q and K rows
+// in that XCD's L2.
+__device__ __forceinline__ void tile_of(int wg, int ntq, int ntk, int& tq, int& tk) {
+  const int total = ntq * ntk;
   int logical = wg;
   if (total % 8 == 0) logical = (wg % 8) * (total / 8) + wg / 8;
-  constexpr int kGroup = 8;
-  const int group_span = kGroup * ntiles;
-  const int g = logical / group_span;
+  constexpr int kGroup = 4;
+  const int span = kGroup * ntk;
+  const int g = logical / span;
   const int first = g * kGroup;
-  const int rows = min(kGroup, ntiles - first);
-  const int in_group = logical % group_span;
+  const int rows = min(kGroup, ntq - first);
+  const int in_group = logical - g * span;
   tq = first + in_group % rows;
   tk = in_group / rows;
 }
@@ -92,22 +104,59 @@ __device__ __forceinline__ void tile_of(int wg, int ntiles, int& tq, int& tk) {
 template <int HD, int MODE, int BLK>
 __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int n_heads, int ldq,
-    int ldk, float out_scale, float* __restrict__ M, int nb, int ntiles) {
-  using C = Cfg<HD>;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kTile * C::kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * C::kRow];
-  // Per (wave, MFMA sub-tile) partial block values; HEADMAX keeps one per head.
-  constexpr int kParts = (MODE == 0) ? 1 : kMaxHeadsHeadmax;
-  __shared__ float part[16][kParts];
+    int ldk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
+  constexpr int kCPH = HD / kChunk;                      // chunks per head
+  constexpr int kParts = (MODE == 1 && BLK == 128) ? kMaxHeadsHeadmax : 1;
+  __shared__ float part[kWaves][kParts];                 // HEADMAX, 128-row blocks: per-head wave maxima
+  __shared__ float fin[kWaves * 4];                      // final per-(wave, sub-tile) values
 
   int tq, tk;
-  tile_of(blockIdx.x, ntiles, tq, tk);
-  const int q0 = tq * kTile, k0 = tk * kTile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  tile_of(blockIdx.x, ntq, ntk, tq, tk);
+  const int q0 = tq * kTQ, k0 = tk * kTK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave >> 1, wk = wave & 1;
-  const int l32 = lane & 31, lhi = lane >> 5;
-  // A sub-tile holds i == j pairs only if its query and key row ranges coincide.
+  const int l32 = lane & 31, hi = lane >> 5;
   const bool diag_wave = (q0 + wq * 64) == (k0 + wk * 64);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)g_stage;
+
+  // ---- per-lane DMA byte offsets: instruction i of this wave fills LDS
+  // pieces P = (i*8 + wave)*64 + lane of the Q (i < kDmaQ) or K region, i.e.
+  // row P/8 and physical piece P%8, which holds logical piece (P%8) ^ swz(row).
+  uint32_t voff[kDmaPerChunk];
+#pragma unroll
+  for (int i = 0; i < kDmaPerChunk; ++i) {
+    const bool is_q = i < kDmaQ;
+    const int ii = is_q ? i : i - kDmaQ;
+    const int r = (ii * kWaves + wave) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(r);
+    const int grow = min((is_q ? q0 : k0) + r, n_tokens - 1);   // rows past N: any valid row
+    voff[i] = (uint32_t)(((size_t)grow * (is_q ? ldq : ldk) + piece * 8) * 2);
+  }
+  // loads of chunk c (head h, part kc) into stage `stage`
+  auto issue = [&](int h, int kc, int stage) {
+    const int col = h * HD + kc * kChunk;
+    const uint16_t* qb = Q + col;
+    const uint16_t* kb = K + col;
+    const uint32_t base = lds0 + (uint32_t)(stage * kStageBytes);
+#pragma unroll
+    for (int i = 0; i < kDmaPerChunk; ++i) {
+      const bool is_q = i < kDmaQ;
+      const int ii = is_q ? i : i - kDmaQ;
+      dma16(is_q ? (const void*)qb : (const void*)kb, voff[i],
+            base + (is_q ? 0u : (uint32_t)kStageQ) + (uint32_t)((ii * kWaves + wave) * 1024));
+    }
+  };
+
+  // ---- per-lane LDS read offsets (bytes from g_stage, stage 0) for the four
+  // k-steps of a chunk; every operand row this lane reads has r & 15 == l32 & 15.
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int piece = (2 * s + hi) ^ swz(l32);
+    offA[s] = (uint32_t)((wq * 64 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
+  }
 
   lemo_f32x16 sum[2][2];
 #pragma unroll
@@ -116,51 +165,61 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum[a][b][e] = 0.f;
+  float total[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // HEADMAX, blocks <= 64 rows: sum over heads
 
-  uint4 vq[C::kPerThread], vk[C::kPerThread];
-  load_head<HD>(Q, ldq, q0, n_tokens, 0, vq);
-  load_head<HD>(K, ldk, k0, n_tokens, 0, vk);
+  const int nchunks = n_heads * kCPH;
+  issue(0, 0, 0);
+  if (nchunks > 1) issue(1 / kCPH, 1 % kCPH, 1);
 
-  for (int h = 0; h < n_heads; ++h) {
-    store_head<HD>(sQ, vq);
-    store_head<HD>(sK, vk);
-    __syncthreads();
-    if (h + 1 < n_heads) {  // prefetch the next head while this one multiplies
-      load_head<HD>(Q, ldq, q0, n_tokens, (h + 1) * HD, vq);
-      load_head<HD>(K, ldk, k0, n_tokens, (h + 1) * HD, vk);
-    }
+  // One head: its kCPH chunks, then the head's epilogue.  U is the head's
+  // position in a group of 3 heads, which fixes every chunk's stage at
+  // compile time (3 stages; a group spans a multiple of 3 chunks).
+  auto do_head = [&](auto U_, int h) {
+    constexpr int U = decltype(U_)::value;
     lemo_f32x16 acc[2][2];
 #pragma unroll
-    for (int ks = 0; ks < HD / 16; ++ks) {
-      lemo_bf16x8 fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const lemo_bf16x8*>(sQ + (wq * 64 + i * 32 + l32) * C::kRow + ks * 16 + lhi * 8);
-        fb[i] = *reinterpret_cast<const lemo_bf16x8*>(sK + (wk * 64 + i * 32 + l32) * C::kRow + ks * 16 + lhi * 8);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          if (ks == 0) {
-            if (MODE == 0)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], sum[a][b], 0, 0, 0);
-            else
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], lemo_f32x16{}, 0, 0, 0);
-          } else {
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
-          }
-        }
-    }
-    __syncthreads();  // LDS is rewritten at the top of the next head
+    for (int kc = 0; kc < kCPH; ++kc) {
+      const int c = h * kCPH + kc;
+      const int stage = (U * kCPH + kc) % kStages;
+      static_assert(kDmaPerChunk == 6, "the vmcnt below assumes 6 loads per chunk");
+      if (c + 1 < nchunks)
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");   // chunk c landed; chunk c+1 may be in flight
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (c + 2 < nchunks) issue((c + 2) / kCPH, (c + 2) % kCPH, (stage + 2) % kStages);
 
+      const uint8_t* st = g_stage + stage * kStageBytes;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        lemo_bf16x8 fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          fa[i] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + i * 32 * kRowBytes);
+          fb[i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            if (kc == 0 && s == 0)  // first k-step of a head: PAPER starts from the running sum, HEADMAX from 0
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], MODE == 0 ? sum[a][b] : lemo_f32x16{},
+                                                                  0, 0, 0);
+            else
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+          }
+      }
+    }
+
+    // head complete
     if (MODE == 0) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) sum[a][b][e] = fmaxf(acc[a][b][e], sum[a][b][e]);
+          for (int e = 0; e < 16; ++e)
+            sum[a][b][e] = __int_as_float(imax(__float_as_int(acc[a][b][e]), __float_as_int(sum[a][b][e])));
     } else {
       if (diag_wave) {
 #pragma unroll
@@ -170,30 +229,40 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
             if (acc_row(lane, e) == l32) acc[a][a][e] = 0.f;
       }
       if (BLK >= 64) {
-        float m = -INFINITY;
+        int m = 0;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) m = fmaxf(m, acc[a][b][e]);
-        m = lemo_wave_max(m);
-        if (lane == 0) part[wave * 4][h] = m;
+            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+        m = wave_imax(m);
+        if (BLK == 128) {
+          if (lane == 0) part[wave][h] = __int_as_float(m);
+        } else {
+          total[0][0] += __int_as_float(m);
+        }
       } else {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            float m = -INFINITY;
+            int m = 0;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) m = fmaxf(m, acc[a][b][e]);
-            m = lemo_wave_max(m);
-            if (lane == 0) part[wave * 4 + a * 2 + b][h] = m;
+            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+            total[a][b] += __int_as_float(wave_imax(m));
           }
       }
     }
+  };
+
+  for (int h0 = 0; h0 < n_heads; h0 += 3) {
+    do_head(std::integral_constant<int, 0>{}, h0);
+    if (h0 + 1 < n_heads) do_head(std::integral_constant<int, 1>{}, h0 + 1);
+    if (h0 + 2 < n_heads) do_head(std::integral_constant<int, 2>{}, h0 + 2);
   }
 
+  // ---- per-(wave, sub-tile) block values -> fin[]
   if (MODE == 0) {
     if (diag_wave) {
 #pragma unroll
@@ -203,56 +272,63 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
           if (acc_row(lane, e) == l32) sum[a][a][e] = 0.f;
     }
     if (BLK >= 64) {
-      float m = 0.f;
+      int m = 0;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) m = fmaxf(m, sum[a][b][e]);
-      m = lemo_wave_max(m);
-      if (lane == 0) part[wave * 4][0] = m;
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(sum[a][b][e]));
+      m = wave_imax(m);
+      if (lane == 0) fin[wave * 4] = __int_as_float(m);
     } else {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          float m = 0.f;
+          int m = 0;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) m = fmaxf(m, sum[a][b][e]);
-          m = lemo_wave_max(m);
-          if (lane == 0) part[wave * 4 + a * 2 + b][0] = m;
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(sum[a][b][e]));
+          m = wave_imax(m);
+          if (lane == 0) fin[wave * 4 + a * 2 + b] = __int_as_float(m);
         }
+    }
+  } else if (BLK == 64) {
+    if (lane == 0) fin[wave * 4] = total[0][0];
+  } else if (BLK == 32) {
+    if (lane == 0) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) fin[wave * 4 + a * 2 + b] = total[a][b];
     }
   }
   __syncthreads();
 
-  // Combine the parts that fall in each block of this tile and write M.
-  constexpr int kPerDim = kTile / BLK;  // blocks per tile side
-  if (tid < kPerDim * kPerDim) {
-    const int lq = tid / kPerDim, lk = tid % kPerDim;
+  // ---- combine the parts of each block of this tile and write M
+  constexpr int kBQ = kTQ / BLK, kBK = kTK / BLK;   // blocks per tile side
+  if (tid < kBQ * kBK) {
+    const int lq = tid / kBK, lk = tid % kBK;
     const int bq = q0 / BLK + lq, bk = k0 / BLK + lk;
     if (bq < nb && bk < nb) {
-      // parts that cover this block: wave (wq, wk) sub-tile (a, b) covers
-      // query rows wq*64 + a*32 and key rows wk*64 + b*32 of the tile
       float val = 0.f;
-      if (MODE == 0) {
-        for (int p = 0; p < 16; ++p) {
+      if (MODE == 1 && BLK == 128) {
+        // waves (wq, wk) with wq / 2 == lq cover this block; heads summed in order
+        for (int h = 0; h < n_heads; ++h) {
+          float m = 0.f;
+          for (int w = 0; w < kWaves; ++w)
+            if (((w >> 1) >> 1) == lq) m = fmaxf(m, part[w][h]);
+          val += m;
+        }
+      } else {
+        // sub-tile (a, b) of wave (wq, wk) covers query rows wq*64 + a*32 and
+        // key rows wk*64 + b*32 of the tile; PAPER takes the max of the parts,
+        // HEADMAX (blocks <= 64 rows) has exactly one part per block
+        for (int p = 0; p < kWaves * 4; ++p) {
           const int w = p >> 2, a = (p >> 1) & 1, b = p & 1;
           if (BLK >= 64 && (a | b)) continue;
           const int rq = ((w >> 1) * 64 + a * 32) / BLK, rk = ((w & 1) * 64 + b * 32) / BLK;
-          if (rq == lq && rk == lk) val = fmaxf(val, part[p][0]);
-        }
-      } else {
-        for (int h = 0; h < n_heads; ++h) {
-          float m = -INFINITY;
-          for (int p = 0; p < 16; ++p) {
-            const int w = p >> 2, a = (p >> 1) & 1, b = p & 1;
-            if (BLK >= 64 && (a | b)) continue;
-            const int rq = ((w >> 1) * 64 + a * 32) / BLK, rk = ((w & 1) * 64 + b * 32) / BLK;
-            if (rq == lq && rk == lk) m = fmaxf(m, part[p][h]);
-          }
-          val += fmaxf(m, 0.f);
+          if (rq == lq && rk == lk) val = fmaxf(val, fin[p]);
         }
       }
       M[(size_t)bq * nb + bk] = val * out_scale;
@@ -260,23 +336,45 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   }
 }
 
-__global__ void k_colsum(const float* __restrict__ M, int nb, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= nb) return;
+// Column sums I[c] = sum_r M[r][c].  A workgroup owns 16 columns; its 256
+// threads split the rows into 16 interleaved slices (thread (slice, column)
+// adds rows slice, slice+16, ... in order), then one thread per column adds
+// the 16 slice sums in slice order.  Fixed order, so the result is
+// deterministic.
+__global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ M, int nb, float* __restrict__ out) {
+  __shared__ float partial[16][17];
+  const int col = blockIdx.x * 16 + (threadIdx.x & 15);
+  const int slice = threadIdx.x >> 4;
   float s = 0.f;
-  for (int r = 0; r < nb; ++r) s += M[(size_t)r * nb + c];
-  out[c] = s;
+  if (col < nb) {
+#pragma unroll 4
+    for (int r = slice; r < nb; r += 16) s += M[(size_t)r * nb + col];
+  }
+  partial[slice][threadIdx.x & 15] = s;
+  __syncthreads();
+  if (threadIdx.x < 16 && blockIdx.x * 16 + threadIdx.x < nb) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += partial[i][threadIdx.x];
+    out[blockIdx.x * 16 + threadIdx.x] = t;
+  }
 }
 
 template <int HD, int MODE>
 hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n, int h, int ldq, int ldk, int block,
                           float scale, float* m, int nb, hipStream_t st) {
-  const int ntiles = (n + kTile - 1) / kTile;
-  const dim3 grid(ntiles * ntiles), blk(kThreads);
+  const int ntq = (n + kTQ - 1) / kTQ, ntk = (n + kTK - 1) / kTK;
+  const dim3 grid(ntq * ntk), blk(kThreads);
   switch (block) {
-    case 32: hipLaunchKernelGGL((k_block_scores<HD, MODE, 32>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntiles); break;
-    case 64: hipLaunchKernelGGL((k_block_scores<HD, MODE, 64>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntiles); break;
-    default: hipLaunchKernelGGL((k_block_scores<HD, MODE, 128>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntiles); break;
+    case 32:
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 32>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      break;
+    case 64:
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 64>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      break;
+    default:
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 128>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      break;
   }
   return hipGetLastError();
 }
@@ -284,7 +382,7 @@ hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n, int h, in
 }  // namespace
 
 hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_colsum, dim3((nb + 255) / 256), dim3(256), 0, stream, m, nb, out);
+  hipLaunchKernelGGL(k_colsum, dim3((nb + 15) / 16), dim3(256), 0, stream, m, nb, out);
   return hipGetLastError();
 }
 
