@@ -6,15 +6,18 @@
 // block score is I[m] = sum_n M[n][m].  Pairs i == j are excluded.
 //
 // Work decomposition
-//   One workgroup (8 waves) owns a 256 x 128 tile of (query rows, key rows)
-//   and walks every head.  Each wave multiplies a 64 x 64 sub-tile with
-//   v_mfma_f32_32x32x16_bf16 (2 x 2 MFMA tiles, fp32 accumulators in VGPRs).
-//   The head dimension is streamed in 64-wide chunks through a 3-stage LDS
-//   ring filled by direct global->LDS loads (global_load_lds_dwordx4), so the
-//   loads of chunk c+2 are in flight while chunk c multiplies; one barrier per
-//   chunk.  LDS rows are 128 B; the 16-B pieces of row r are stored XOR-
-//   swizzled (piece p at p ^ swz(r)) so that the MFMA operand reads (32 rows,
-//   one piece each) hit distinct banks.
+//   A workgroup of 4 waves owns a 128 x 128 tile of (query rows, key rows)
+//   and walks every head; two workgroups share each CU.  Each wave multiplies
+//   a 64 x 64 sub-tile with v_mfma_f32_32x32x16_bf16 (2 x 2 MFMA tiles, fp32
+//   accumulators in VGPRs).  The head dimension is streamed in 64-wide chunks
+//   through a 2-stage LDS ring (64 KiB per workgroup) filled by direct
+//   global->LDS loads (global_load_lds_dwordx4): chunk c+1 loads while chunk c
+//   multiplies, one barrier per chunk.  The two workgroups on a CU have
+//   independent barriers, so one's barrier/restart bubbles are filled by the
+//   other's MFMAs.  LDS rows are 128 B; the 16-B pieces of row r are stored
+//   XOR-swizzled (piece p at p ^ swz(r)) so that the MFMA operand reads (32
+//   rows, one piece each) hit distinct banks.  Operand reads run one k-step
+//   ahead of the MFMAs.
 //
 // The score tile never leaves registers:
 //   PAPER   (heads first, then block max): each head's MFMA chain starts from
@@ -40,18 +43,18 @@
 
 namespace {
 
-constexpr int kTQ = 256;        // query rows per workgroup
+constexpr int kTQ = 128;        // query rows per workgroup
 constexpr int kTK = 128;        // key rows per workgroup
-constexpr int kWaves = 8;       // 4 (query) x 2 (key) waves of 64 x 64
+constexpr int kWaves = 4;       // 2 (query) x 2 (key) waves of 64 x 64
 constexpr int kThreads = kWaves * 64;
 constexpr int kChunk = 64;      // head-dim elements per pipeline stage
-constexpr int kRowBytes = kChunk * 2;
-constexpr int kStageQ = kTQ * kRowBytes;           // 32 KiB
+constexpr int kRowBytes = kChunk * 2;              // 128 B: eight 16-B pieces
+constexpr int kStageQ = kTQ * kRowBytes;           // 16 KiB
 constexpr int kStageK = kTK * kRowBytes;           // 16 KiB
-constexpr int kStageBytes = kStageQ + kStageK;     // 48 KiB
-constexpr int kStages = 3;
+constexpr int kStageBytes = kStageQ + kStageK;     // 32 KiB
+constexpr int kStages = 2;                         // 64 KiB per workgroup: two workgroups per CU
 constexpr int kDmaQ = kStageQ / (kThreads * 16);   // 4 loads of 16 B per thread
-constexpr int kDmaK = kStageK / (kThreads * 16);   // 2
+constexpr int kDmaK = kStageK / (kThreads * 16);   // 4
 constexpr int kDmaPerChunk = kDmaQ + kDmaK;
 constexpr int kMaxHeadsHeadmax = 128;
 
@@ -91,7 +94,7 @@ __device__ __forceinline__ void tile_of(int wg, int ntq, int ntk, int& tq, int& 
   const int total = ntq * ntk;
   int logical = wg;
   if (total % 8 == 0) logical = (wg % 8) * (total / 8) + wg / 8;
-  constexpr int kGroup = 4;
+  constexpr int kGroup = 8;
   const int span = kGroup * ntk;
   const int g = logical / span;
   const int first = g * kGroup;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   const uint32_t lds0 = (uint32_t)(uintptr_t)g_stage;
 
   // ---- per-lane DMA byte offsets: instruction i of this wave fills LDS
-  // pieces P = (i*8 + wave)*64 + lane of the Q (i < kDmaQ) or K region, i.e.
+  // pieces P = (i*kWaves + wave)*64 + lane of the Q (i < kDmaQ) or K region, i.e.
   // row P/8 and physical piece P%8, which holds logical piece (P%8) ^ swz(row).
   uint32_t voff[kDmaPerChunk];
 #pragma unroll
@@ -158,7 +161,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     offB[s] = (uint32_t)(kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
   }
 
-  lemo_f32x16 sum[2][2];
+  lemo_f32x16 sum[2][2];          // PAPER: running sum over heads of max(0, S^h)
+  lemo_f32x16 acc[2][2][2];       // [head parity][sub-tile]: S^h of the current and previous head
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -166,100 +170,126 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum[a][b][e] = 0.f;
   float total[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // HEADMAX, blocks <= 64 rows: sum over heads
+  int hm_lane = 0;                                // HEADMAX, blocks >= 64: this lane's running block max
+
+  // Folds sub-tile t = (a, b) of a finished head (accumulators acc[P]) into
+  // the cross-head state.  Runs interleaved with the next head's MFMAs.
+  auto finalize = [&](auto P_, int t, int h) {
+    constexpr int P = decltype(P_)::value;
+    const int a = t >> 1, b = t & 1;
+    if (MODE == 0) {
+      // sum += max(0, S): the bit pattern of a negative float is a negative
+      // integer, so v_max_i32 against 0 is the ReLU
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
+    } else {
+      if (diag_wave && a == b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(lane, e) == l32) acc[P][a][b][e] = 0.f;
+      }
+      int m = BLK >= 64 ? hm_lane : 0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[P][a][b][e]));
+      if (BLK >= 64) {
+        hm_lane = m;
+        if (t == 3) {  // all four sub-tiles lie in one block: reduce across lanes
+          m = wave_imax(m);
+          hm_lane = 0;
+          if (BLK == 128) {
+            if (lane == 0) part[wave][h] = __int_as_float(m);
+          } else {
+            total[0][0] += __int_as_float(m);
+          }
+        }
+      } else {
+        total[a][b] += __int_as_float(wave_imax(m));
+      }
+    }
+  };
 
   const int nchunks = n_heads * kCPH;
-  issue(0, 0, 0);
-  if (nchunks > 1) issue(1 / kCPH, 1 % kCPH, 1);
+  lemo_bf16x8 fa[2][2], fb[2][2];   // operand fragments, [k-step buffer][sub-tile]
+  auto read_frags = [&](int buf, const uint8_t* st, int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + i * 32 * kRowBytes);
+      fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
+    }
+  };
 
-  // One head: its kCPH chunks, then the head's epilogue.  U is the head's
-  // position in a group of 3 heads, which fixes every chunk's stage at
-  // compile time (3 stages; a group spans a multiple of 3 chunks).
-  auto do_head = [&](auto U_, int h) {
-    constexpr int U = decltype(U_)::value;
-    lemo_f32x16 acc[2][2];
+  issue(0, 0, 0);
+
+  // One head h into acc[P].  Each chunk step: this wave's loads of chunk c
+  // have landed (nothing newer is in flight), then a workgroup barrier, after
+  // which chunk c is complete in LDS and every wave has consumed chunk c-1
+  // (its operands are in registers), so the other stage is refilled with
+  // chunk c+1 while chunk c is multiplied.  The barrier is a plain s_barrier:
+  // no LDS fence is needed, since no wave reads LDS that another wave wrote.
+  // Two workgroups share each CU; their barriers are independent, so one
+  // workgroup's barrier and restart bubbles are filled by the other's MFMAs.
+  // During the head's first chunk the previous head (acc[1-P]) is folded in
+  // (HEADMAX), one sub-tile per k-step, under the MFMAs.
+  auto do_head = [&](auto P_, int h) {
+    constexpr int P = decltype(P_)::value;
 #pragma unroll
     for (int kc = 0; kc < kCPH; ++kc) {
       const int c = h * kCPH + kc;
-      const int stage = (U * kCPH + kc) % kStages;
-      static_assert(kDmaPerChunk == 6, "the vmcnt below assumes 6 loads per chunk");
-      if (c + 1 < nchunks)
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");   // chunk c landed; chunk c+1 may be in flight
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (c + 2 < nchunks) issue((c + 2) / kCPH, (c + 2) % kCPH, (stage + 2) % kStages);
-
-      const uint8_t* st = g_stage + stage * kStageBytes;
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 1 < nchunks) issue((c + 1) / kCPH, (c + 1) % kCPH, (c + 1) % kStages);
+      const uint8_t* st = g_stage + (c % kStages) * kStageBytes;
+      read_frags(0, st, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        lemo_bf16x8 fa[2], fb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          fa[i] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + i * 32 * kRowBytes);
-          fb[i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
-        }
+        const int cur = s & 1;
+        // operand reads run one k-step ahead of the MFMAs; the scheduling
+        // fences keep the compiler from folding the two buffers into one
+        if (s + 1 < 4) read_frags(cur ^ 1, st, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             if (kc == 0 && s == 0)  // first k-step of a head: PAPER starts from the running sum, HEADMAX from 0
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], MODE == 0 ? sum[a][b] : lemo_f32x16{},
-                                                                  0, 0, 0);
+              acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b],
+                                                                     MODE == 0 ? sum[a][b] : lemo_f32x16{}, 0, 0, 0);
             else
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+              acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[P][a][b], 0, 0, 0);
           }
+        if (MODE == 1 && kc == 0 && h > 0) finalize(std::integral_constant<int, 1 - P>{}, s, h - 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // head complete
     if (MODE == 0) {
+      // acc = sum + S^h; sum >= 0 and a negative float is a negative integer,
+      // so sum = max(acc, sum) = sum + max(0, S^h) is one v_max_i32
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            sum[a][b][e] = __int_as_float(imax(__float_as_int(acc[a][b][e]), __float_as_int(sum[a][b][e])));
-    } else {
-      if (diag_wave) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (acc_row(lane, e) == l32) acc[a][a][e] = 0.f;
-      }
-      if (BLK >= 64) {
-        int m = 0;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
-        m = wave_imax(m);
-        if (BLK == 128) {
-          if (lane == 0) part[wave][h] = __int_as_float(m);
-        } else {
-          total[0][0] += __int_as_float(m);
-        }
-      } else {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            int m = 0;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
-            total[a][b] += __int_as_float(wave_imax(m));
-          }
-      }
+            sum[a][b][e] = __int_as_float(imax(__float_as_int(acc[P][a][b][e]), __float_as_int(sum[a][b][e])));
     }
   };
 
-  for (int h0 = 0; h0 < n_heads; h0 += 3) {
-    do_head(std::integral_constant<int, 0>{}, h0);
-    if (h0 + 1 < n_heads) do_head(std::integral_constant<int, 1>{}, h0 + 1);
-    if (h0 + 2 < n_heads) do_head(std::integral_constant<int, 2>{}, h0 + 2);
+  if (MODE == 0) {
+    for (int h = 0; h < n_heads; ++h) do_head(std::integral_constant<int, 0>{}, h);
+  } else {
+    int h = 0;
+    for (; h + 1 < n_heads; h += 2) {
+      do_head(std::integral_constant<int, 0>{}, h);
+      do_head(std::integral_constant<int, 1>{}, h + 1);
+    }
+    if (h < n_heads) {
+      do_head(std::integral_constant<int, 0>{}, h);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) finalize(std::integral_constant<int, 0>{}, t, h);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) finalize(std::integral_constant<int, 1>{}, t, h - 1);
+    }
   }
 
   // ---- per-(wave, sub-tile) block values -> fin[]
@@ -317,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
         for (int h = 0; h < n_heads; ++h) {
           float m = 0.f;
           for (int w = 0; w < kWaves; ++w)
-            if (((w >> 1) >> 1) == lq) m = fmaxf(m, part[w][h]);
+            if ((w >> 1) * 64 / BLK == lq) m = fmaxf(m, part[w][h]);
           val += m;
         }
       } else {
