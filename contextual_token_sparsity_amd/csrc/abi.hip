@@ -117,6 +117,8 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
   REQUIRE(rank % 32 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 32, at most 256)", rank);
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
+  REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
+          "predictor matrices must be 16-byte aligned");
   const size_t need = lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
   REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
           "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);

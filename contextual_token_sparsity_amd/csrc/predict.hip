@@ -11,7 +11,7 @@
 //                 split over s = slices Ks of d_model so that ~1000 waves run)
 //   k_project     hid = bf16(max(0, sum_s part[s])) (fixed slice order), then
 //                 q_hat = hid_q V_q, k_hat = hid_k V_k in fp32
-//   k_pair        M_hat[m][n] = max(0, q_hat[m] . k_hat[n])  (fp32)
+//   k_pair        M_hat[m][n] = max(0, q_hat[m] . k_hat[n])  (fp32, 16 x 16 tiles)
 //   k_colsum      I_hat[n] = sum_m M_hat[m][n]
 #include "lemo_internal.h"
 
@@ -99,6 +99,7 @@ __global__ __launch_bounds__(512) void k_project(const float* __restrict__ part,
   const int m = blockIdx.x, t = threadIdx.x;
   const int width = 2 * rank;
   float h = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nslices; ++s) h += part[((size_t)s * nb + m) * width + t];
   h = fmaxf(h, 0.f);
   hid[t] = lemo_bf16_to_f32(lemo_f32_to_bf16(h));
@@ -107,44 +108,43 @@ __global__ __launch_bounds__(512) void k_project(const float* __restrict__ part,
   const int v = is_q ? t : t - rank;
   const uint16_t* V = is_q ? vq : vk;
   const float* hh = hid + (is_q ? 0 : rank);
+  // the V column is read 16 rows at a time so its loads overlap; the sum
+  // still runs over u in order
   float acc = 0.f;
-  for (int u = 0; u < rank; ++u) acc = fmaf(hh[u], lemo_bf16_to_f32(V[(size_t)u * rank + v]), acc);
+  for (int u0 = 0; u0 < rank; u0 += 16) {
+    float vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vv[j] = lemo_bf16_to_f32(V[(size_t)(u0 + j) * rank + v]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc = fmaf(hh[u0 + j], vv[j], acc);
+  }
   (is_q ? qhat : khat)[(size_t)m * rank + v] = acc;
 }
 
 // ------------------------------------------------------------ pair scores
-// 32 x 32 tile of M_hat per workgroup; q_hat / k_hat rows staged in LDS in
-// 64-wide slices of the rank; each thread owns a 2 x 2 patch of outputs.
+// 16 x 16 tile of M_hat per workgroup, one output per thread; q_hat / k_hat
+// rows staged in LDS in 64-wide slices of the rank; the dot runs over v in
+// order.
 __global__ __launch_bounds__(256) void k_pair(const float* __restrict__ qhat, const float* __restrict__ khat,
                                               int nb, int rank, float* __restrict__ M) {
-  __shared__ float sq[32][65];
-  __shared__ float sk[32][65];
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  __shared__ float sq[16][65];
+  __shared__ float sk[16][65];
+  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
   const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  for (int u0 = 0; u0 < rank; u0 += 64) {
-    for (int i = t; i < 32 * 64; i += 256) {
+  float acc = 0.f;
+  for (int v0 = 0; v0 < rank; v0 += 64) {
+    for (int i = t; i < 16 * 64; i += 256) {
       const int r = i >> 6, c = i & 63;
-      const bool in_rank = u0 + c < rank;   // rank is a multiple of 32, the slice is 64 wide
-      sq[r][c] = (m0 + r < nb && in_rank) ? qhat[(size_t)(m0 + r) * rank + u0 + c] : 0.f;
-      sk[r][c] = (n0 + r < nb && in_rank) ? khat[(size_t)(n0 + r) * rank + u0 + c] : 0.f;
+      const bool in = v0 + c < rank;   // rank is a multiple of 32, the slice is 64 wide
+      sq[r][c] = (m0 + r < nb && in) ? qhat[(size_t)(m0 + r) * rank + v0 + c] : 0.f;
+      sk[r][c] = (n0 + r < nb && in) ? khat[(size_t)(n0 + r) * rank + v0 + c] : 0.f;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int u = 0; u < 64; ++u)
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = fmaf(sq[ty * 2 + a][u], sk[tx * 2 + b][u], acc[a][b]);
+#pragma unroll 16
+    for (int v = 0; v < 64; ++v) acc = fmaf(sq[ty][v], sk[tx][v], acc);
     __syncthreads();
   }
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int m = m0 + ty * 2 + a, n = n0 + tx * 2 + b;
-      if (m < nb && n < nb) M[(size_t)m * nb + n] = fmaxf(acc[a][b], 0.f);
-    }
+  if (m0 + ty < nb && n0 + tx < nb) M[(size_t)(m0 + ty) * nb + n0 + tx] = fmaxf(acc, 0.f);
 }
 
 struct Layout {
@@ -200,7 +200,7 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
   hipLaunchKernelGGL(k_hidden, dim3((n_mt * n_nt + 3) / 4, s), dim3(256), 0, st, xbar, d_model, nb, u_q, u_k,
                      rank, d_model / s, n_mt, part);
   hipLaunchKernelGGL(k_project, dim3(nb), dim3(2 * rank), 0, st, part, s, nb, rank, v_q, v_k, qhat, khat);
-  hipLaunchKernelGGL(k_pair, dim3((nb + 31) / 32, (nb + 31) / 32), dim3(256), 0, st, qhat, khat, nb, rank, M);
+  hipLaunchKernelGGL(k_pair, dim3((nb + 15) / 16, (nb + 15) / 16), dim3(256), 0, st, qhat, khat, nb, rank, M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return lemo_launch_colsum(M, nb, scores, st);
