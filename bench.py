@@ -18,7 +18,6 @@ the timed region.  Reported value: tokens scored + eliminated per second.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,6 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "llama2-7b-n16k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_scores_llama2-7b-n16k_traffic.json")
+CLOCK_SETTLE_S = 0.3
 
 
 def parse():
@@ -48,14 +48,10 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "contextual_token_sparsity_amd", "csrc", "block_scores.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
-
-
 def load_traffic():
     """HBM bytes per launch of the exact-score kernel from committed counter
     runs, only if they were taken on the current kernel source."""
+    from contextual_token_sparsity_amd.rocprof_summary import kernel_source_hash
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -134,7 +130,15 @@ def main():
         if timed:
             mark("scatter1")
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    # The GPU clock ramps up under sustained load; run untimed steps for at
+    # least CLOCK_SETTLE_S first so the timed steps see the steady-state clock.
+    print(f"[bench] clock settle {CLOCK_SETTLE_S} s, then warmup {args.warmup}", file=sys.stderr, flush=True)
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while time.perf_counter() - t_settle < CLOCK_SETTLE_S:
+        step(False)
+        torch.cuda.synchronize()
+        settle_steps += 1
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -203,6 +207,7 @@ def main():
         "movement_GBps": move_bytes / ((stages["gather_pad_x_and_act"] + stages["scatter_residual"]) * 1e-3) / 1e9,
         "dev_status": st,
         "host_wall_s": host_s,
+        "clock_settle_steps": settle_steps,
     }
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)

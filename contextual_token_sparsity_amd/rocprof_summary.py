@@ -1,0 +1,107 @@
+"""Turns rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    # kernel durations (rocprofv3 --kernel-trace --stats ... -o trace)
+    python -m contextual_token_sparsity_amd.rocprof_summary trace STATS_CSV OUT_TXT "COMMAND"
+
+    # HBM bytes per launch of the exact-score kernel from two counter runs
+    # (rocprofv3 --pmc FETCH_SIZE / --pmc WRITE_SIZE of `bench.py --copy-probe`)
+    python -m contextual_token_sparsity_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_TXT "COMMANDS"
+
+The counters are calibrated on the plain 1 GiB device-to-device copy that
+`bench.py --copy-probe` issues: the ratio of its known bytes to what each
+counter reports scales the exact-score kernel's readings.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+SCORE_KERNEL = "k_block_scores"
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(PKG, "csrc", "block_scores.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def trace(stats_csv: str, out_txt: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "",
+             f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'% time':>7}"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) <= 72 else name[:69] + "..."
+        lines.append(f"{short:<72} {r['Calls']:>6} {float(r['AverageNs']) / 1e3:>10.1f} "
+                     f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
+                     f"{float(r['Percentage']):>7.2f}")
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_kernel(counter_csv: str):
+    rows = list(csv.DictReader(open(counter_csv)))
+    vals = defaultdict(list)
+    copies = []
+    for r in rows:
+        v = float(r["Counter_Value"])
+        name = r["Kernel_Name"]
+        if SCORE_KERNEL in name:
+            vals["score"].append(v)
+        elif "copyBuffer" in name:
+            copies.append((v, int(r["Grid_Size"])))
+    return vals["score"], copies
+
+
+def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, commands: str) -> None:
+    f_score, f_copy = _per_kernel(fetch_csv)
+    w_score, w_copy = _per_kernel(write_csv)
+    if not (f_score and w_score and f_copy and w_copy):
+        raise SystemExit("missing score-kernel or copy-probe dispatches in the counter files")
+    # the copy probe is the copyBuffer dispatch with the largest reading
+    # (uploads of the inputs are host-to-device and smaller)
+    f_ref = max(f_copy)[0]
+    w_ref = max(w_copy)[0]
+    f_scale = COPY_BYTES / (f_ref * 1024.0)
+    w_scale = COPY_BYTES / (w_ref * 1024.0)
+    fetch_b = sum(f_score) / len(f_score) * 1024.0 * f_scale
+    write_b = sum(w_score) / len(w_score) * 1024.0 * w_scale
+    rec = {
+        "kernel": SCORE_KERNEL,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "launches": len(f_score),
+        "commands": commands,
+    }
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(out_txt, "w") as f:
+        f.write("# HBM traffic of the exact-score kernel (rocprofv3 counters)\n")
+        f.write(f"# commands: {commands}\n\n")
+        f.write(f"copy probe (1 GiB device copy): FETCH_SIZE {f_ref:.0f} KiB, WRITE_SIZE {w_ref:.0f} KiB\n")
+        f.write(f"  -> scale factors: fetch x{f_scale:.3f}, write x{w_scale:.3f}\n")
+        f.write(f"{SCORE_KERNEL}: {len(f_score)} launches, FETCH_SIZE avg {sum(f_score) / len(f_score):.0f} KiB, "
+                f"WRITE_SIZE avg {sum(w_score) / len(w_score):.0f} KiB\n")
+        f.write(f"  -> HBM bytes per launch: read {fetch_b / 1e9:.3f} GB, write {write_b / 1e9:.4f} GB, "
+                f"total {(fetch_b + write_b) / 1e9:.3f} GB\n")
+        f.write(f"kernel source sha256[:16]: {kernel_source_hash()}\n")
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1] if len(sys.argv) > 1 else ""
+    if cmd == "trace" and len(sys.argv) == 5:
+        trace(*sys.argv[2:5])
+    elif cmd == "traffic" and len(sys.argv) == 7:
+        traffic(*sys.argv[2:7])
+    else:
+        print(__doc__)
+        sys.exit(2)
