@@ -123,6 +123,8 @@ def main():
         if timed:
             mark("select1")
         lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256, dev_status=status)
+        if timed:
+            mark("gatherx1")
         lemo.lemo_gather_pad(act, b, kept, n_kept, ak, pad_multiple=256, dev_status=status)
         if timed:
             mark("gather1")
@@ -172,7 +174,18 @@ def main():
     achieved = flops / t_scores_s / 1e12
     R = nk * b
     Rp = -(-R // 256) * 256
-    move_bytes = 2 * R * d * 2 + (Rp - R) * d * 2 + 2 * R * wm * 2 + (Rp - R) * wm * 2 + 3 * R * d * 2
+    # algorithmic bytes: a gathered row is read and written once, a pad row
+    # written once; a scattered row reads residual and y and writes residual
+    bytes_gx = 2 * R * d * 2 + (Rp - R) * d * 2
+    bytes_ga = 2 * R * wm * 2 + (Rp - R) * wm * 2
+    bytes_sc = 3 * R * d * 2
+    move_bytes = bytes_gx + bytes_ga + bytes_sc
+    warm_ms = {"gather_x": avg("select1", "gatherx1"), "gather_act": avg("gatherx1", "gather1"),
+               "scatter": stages["scatter_residual"]}
+    cold_ms = movement_cold(lambda: lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256),
+                            lambda: lemo.lemo_gather_pad(act, b, kept, n_kept, ak, pad_multiple=256),
+                            lambda: lemo.lemo_scatter_residual(resid, b, kept, n_kept, y), stream, dev)
+    move_bytes_k = {"gather_x": bytes_gx, "gather_act": bytes_ga, "scatter": bytes_sc}
     out = {
         "metric": METRIC,
         "value": N * args.steps / (total_ms * 1e-3),
@@ -205,6 +218,13 @@ def main():
         "stages_ms": stages,
         "n_kept_blocks": nk,
         "movement_GBps": move_bytes / ((stages["gather_pad_x_and_act"] + stages["scatter_residual"]) * 1e-3) / 1e9,
+        "movement": {
+            kname: {"bytes": move_bytes_k[kname],
+                    "warm_GBps": move_bytes_k[kname] / (warm_ms[kname] * 1e-3) / 1e9,
+                    "cold_GBps": move_bytes_k[kname] / (cold_ms[kname] * 1e-3) / 1e9,
+                    "cold_frac": move_bytes_k[kname] / (cold_ms[kname] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            for kname in ("gather_x", "gather_act", "scatter")},
+        "predictor_path_tokens_per_s": N / (sum(v for kk, v in stages.items() if kk != "block_scores") * 1e-3),
         "dev_status": st,
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
@@ -212,11 +232,37 @@ def main():
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
         dst.copy_(src)
+        c1.record(stream)
         torch.cuda.synchronize()
+        out["copy_probe_GBps"] = 2.0 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, w)
     print(json.dumps(out), flush=True)
+
+
+def movement_cold(gx, ga, sc, stream, dev, reps=5):
+    """Median time (ms) of each movement call with the 256 MB Infinity Cache
+    flushed first (a 512 MiB buffer is overwritten before every launch)."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (("gather_x", gx), ("gather_act", ga), ("scatter", sc)):
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name] = float(np.median(ts))
+    return res
 
 
 def cpu_baseline(L, w):

@@ -87,9 +87,10 @@ __device__ __forceinline__ int wave_imax(int v) {
 
 // Maps a linear workgroup id to a (query tile, key tile) pair.  Dispatch goes
 // round-robin over the 8 XCDs; each XCD gets a contiguous range of logical
-// tiles, walked in groups of 4 query tiles so that the ~32 workgroups
-// resident on one XCD cover a 4 x 8 patch of tiles and share Q and K rows
-// in that XCD's L2.
+// tiles, walked in groups of 8 query tiles so that the 64 workgroups
+// resident on one XCD (2 per CU) cover an 8 x 8 patch of tiles and share Q
+// and K rows in that XCD's L2.  (Groups of 2, 4 or 16 rows, or a serpentine
+// walk, time within 1-2 % of this at N = 16384.)
 __device__ __forceinline__ void tile_of(int wg, int ntq, int ntk, int& tq, int& tk) {
   const int total = ntq * ntk;
   int logical = wg;

@@ -433,3 +433,81 @@ def test_pipeline_tiny(path):
         rows = O.kept_token_rows(kept_r, nk_r, w.block)
         ref_res = O.scatter_residual(L.x, w.block, kept_r, nk_r, L.y[rows])
         assert np.array_equal(host_bits(xd), ref_res)
+
+
+def test_pipeline_13b_four_layer_chain():
+    """Llama2-13B-shaped stack (N=32768, d=5120, block 128, rank 256), four
+    layers chained on the GPU with no host round trip: predicted scores of the
+    current residual stream -> top-k select (keep 60/45/35/25 %) -> gather of
+    the kept rows (the layer's input) -> in-place add of a fresh stand-in
+    layer output.  Each layer is compared with the oracle's own chain; when a
+    layer's mask differs only on near-threshold blocks (allowed), both chains
+    continue from the oracle's residual."""
+    w = synth.WORKLOADS["llama2-13b-n32k-4layer"]
+    N, d, b = w.n_tokens, w.d_model, w.block
+    nb = N // b
+    L0 = synth.make_workload(w, 0)
+    res_ref = L0.x.copy()
+    resd = dev(L0.x)
+    cap = N
+    xin = torch.empty((cap, d), dtype=torch.int16, device="cuda")
+    yk = torch.empty((cap, d), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for layer, pct in enumerate(w.keep_pct):
+        say("13b chain layer", layer, "keep", pct)
+        L = L0 if layer == 0 else synth.make_workload(w, layer)
+        wts = [L.u_q, L.v_q, L.u_k, L.v_k]
+        k = synth.keep_count(pct, nb)
+        # oracle chain
+        _, I_ref, _, _ = O.predict_scores(res_ref, *wts, b)
+        mask_r, kept_r, nk_r, th_r = O.select_mask(I_ref.astype(np.float32), O.SELECT_TOPK, keep_blocks=k)
+        rows = O.kept_token_rows(kept_r, nk_r, b)
+        xin_ref, _ = O.gather_pad(res_ref, b, kept_r, nk_r, np.zeros((cap, d), np.uint16), 256)
+        res_next = O.scatter_residual(res_ref, b, kept_r, nk_r, L.y[rows])
+        # GPU chain
+        I, _ = lemo.lemo_predict_scores(resd, *[dev(a) for a in wts], b)
+        mask, kept, nk, _ = lemo.lemo_select_mask(I, O.SELECT_TOPK, keep_blocks=k, dev_status=status)
+        xin.zero_()
+        lemo.lemo_gather_pad(resd, b, kept, nk, xin, pad_multiple=256, dev_status=status)
+        lemo.lemo_gather_pad(dev(L.y), b, kept, nk, yk, dev_status=status)
+        lemo.lemo_scatter_residual(resd, b, kept, nk, yk, dev_status=status)
+        torch.cuda.synchronize()
+        ok, worst = scores_close(I.cpu().numpy(), I_ref)
+        assert ok, (layer, worst)
+        assert int(nk.item()) == k == nk_r
+        ok, diff = mask_acceptable(mask.cpu().numpy(), mask_r, I_ref, th_r)
+        assert ok, (layer, diff)
+        assert int(status.item()) == 0
+        if diff.size == 0:
+            assert np.array_equal(host_bits(xin), xin_ref), layer
+            assert np.array_equal(host_bits(resd), res_next), layer
+        else:
+            say("layer", layer, "near-threshold mask difference on blocks", diff, "- resyncing")
+            resd.copy_(dev(res_next))
+        res_ref = res_next
+
+
+def test_scatter_every_bf16_pair():
+    """The scatter's arithmetic on all 2^32 pairs of bf16 bit patterns, against
+    torch's float32 add followed by its round-to-nearest-even conversion to
+    bfloat16 (for finite inputs that is the correctly rounded bf16 sum: two
+    bf16 values add exactly in float32 unless one is below half an ulp of the
+    other).  NaN results are compared as NaN, whatever their payload."""
+    rows, width = 256, 65536
+    a = torch.arange(width, dtype=torch.int32, device="cuda").to(torch.int16)
+    res = torch.empty((rows, width), dtype=torch.int16, device="cuda")
+    y = torch.empty_like(res)
+    kept = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nk = torch.ones(1, dtype=torch.int32, device="cuda")
+    bad = torch.zeros((), dtype=torch.int64, device="cuda")
+    for c in range(0, 65536, rows):
+        res.copy_(a.expand(rows, width))
+        bvals = torch.arange(c, c + rows, dtype=torch.int32, device="cuda").to(torch.int16)
+        y.copy_(bvals[:, None].expand(rows, width))
+        ref = (res.view(torch.bfloat16).float() + y.view(torch.bfloat16).float()).to(torch.bfloat16)
+        lemo.lemo_scatter_residual(res, rows, kept, nk, y)
+        got = res.view(torch.bfloat16)
+        both_nan = torch.isnan(got) & torch.isnan(ref)
+        bad += ((res != ref.view(torch.int16)) & ~both_nan).sum()
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
