@@ -13,7 +13,22 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnrollGather = 8;   // rows in flight per thread
+constexpr int kUnrollScatter = 4;
+
+// Streaming 16-byte accesses: every byte is touched once, so the loads and
+// stores carry the nontemporal hint and do not displace other data from L2
+// and the Infinity Cache (measured ~10-20 % faster than plain accesses when
+// the source is not already cached).
+typedef unsigned int lemo_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const lemo_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const lemo_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
+  const lemo_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<lemo_u32x4*>(p));
+}
 
 __device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b) {
   const uint32_t* pa = &a.x;
@@ -55,28 +70,28 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
   const int ch = blockIdx.x * kThreads + threadIdx.x;
   if (ch * 8 >= width) return;
   const int step = gridDim.y;
-  for (int p0 = blockIdx.y; p0 < rows; p0 += step * kUnroll) {
-    uint4 v[kUnroll];
-    int tok[kUnroll];
+  for (int p0 = blockIdx.y; p0 < rows; p0 += step * kUnrollGather) {
+    uint4 v[kUnrollGather];
+    int tok[kUnrollGather];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollGather; ++u) {
       const int p = p0 + u * step;
       v[u] = make_uint4(0, 0, 0, 0);
       tok[u] = -1;
       if (p < n_rows) {
         tok[u] = token_of(kept, p, block, nb);
-        if (tok[u] >= 0) v[u] = *reinterpret_cast<const uint4*>(src + (size_t)tok[u] * ld_src + ch * 8);
+        if (tok[u] >= 0) v[u] = load_stream(src + (size_t)tok[u] * ld_src + ch * 8);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollGather; ++u) {
       const int p = p0 + u * step;
       if (p >= rows) break;
       if (p < n_rows && tok[u] < 0) {
         if (status) atomicOr(status, LEMO_DEV_BAD_KEPT);
         continue;
       }
-      *reinterpret_cast<uint4*>(dst + (size_t)p * ld_dst + ch * 8) = v[u];
+      store_stream(dst + (size_t)p * ld_dst + ch * 8, v[u]);
     }
   }
 }
@@ -95,22 +110,22 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
   const int ch = blockIdx.x * kThreads + threadIdx.x;
   if (ch * 8 >= width) return;
   const int step = gridDim.y;
-  for (int p0 = blockIdx.y; p0 < n_rows; p0 += step * kUnroll) {
-    uint4 r[kUnroll], a[kUnroll];
-    int tok[kUnroll];
+  for (int p0 = blockIdx.y; p0 < n_rows; p0 += step * kUnrollScatter) {
+    uint4 r[kUnrollScatter], a[kUnrollScatter];
+    int tok[kUnrollScatter];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollScatter; ++u) {
       const int p = p0 + u * step;
       tok[u] = p < n_rows ? token_of(kept, p, block, nb) : -2;
       if (tok[u] >= 0) {
-        r[u] = *reinterpret_cast<const uint4*>(res + (size_t)tok[u] * ld_res + ch * 8);
-        a[u] = *reinterpret_cast<const uint4*>(y + (size_t)p * ld_y + ch * 8);
+        r[u] = load_stream(res + (size_t)tok[u] * ld_res + ch * 8);
+        a[u] = load_stream(y + (size_t)p * ld_y + ch * 8);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollScatter; ++u) {
       if (tok[u] >= 0) {
-        *reinterpret_cast<uint4*>(res + (size_t)tok[u] * ld_res + ch * 8) = add_bf16x8(r[u], a[u]);
+        store_stream(res + (size_t)tok[u] * ld_res + ch * 8, add_bf16x8(r[u], a[u]));
       } else if (tok[u] == -1 && status) {
         atomicOr(status, LEMO_DEV_BAD_KEPT);
       }
