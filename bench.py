@@ -246,14 +246,15 @@ def main():
 
 def movement_cold(gx, ga, sc, stream, dev, reps=5):
     """Median time (ms) of each movement call with the 256 MB Infinity Cache
-    flushed first (a 512 MiB buffer is overwritten before every launch)."""
+    flushed first: a 512 MiB buffer is read (not written, so no dirty lines
+    are left to be written back during the timed call) before every launch."""
     import torch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev).view(torch.int64)
     res = {}
     for name, fn in (("gather_x", gx), ("gather_act", ga), ("scatter", sc)):
         ts = []
         for i in range(reps):
-            flush.fill_(i & 0xFF)
+            flush.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
