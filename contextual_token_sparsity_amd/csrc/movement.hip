@@ -133,9 +133,13 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
   }
 }
 
+// Workgroups: one per 4 KiB column stripe (x) times row slots (y).  At least
+// 2048 workgroups in all, and at least 1024 row slots, so that wide rows
+// (e.g. an MLP activation of 11008 columns) keep as many rows in flight as
+// narrow ones.
 dim3 grid_for(int width, int max_rows) {
   const int gx = (width / 8 + kThreads - 1) / kThreads;
-  int gy = (2048 + gx - 1) / gx;
+  int gy = max(1024, (2048 + gx - 1) / gx);
   gy = max(1, min(gy, max_rows));
   return dim3(gx, gy);
 }
