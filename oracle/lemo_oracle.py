@@ -208,6 +208,18 @@ def predict_scores(x, u_q, v_q, u_k, v_k, block: int):
     return M, M.sum(axis=0), q_hat, k_hat
 
 
+def token_embeddings(x, u, v) -> np.ndarray:
+    """Per-token predictor output ([Jenga] 4.2.2, Figure 8 and the complexity
+    analysis: the query and key predictors cost O(s h^2), one pass per token of
+    the sequence).  Reading: the predictor of `predictor_embeddings` applied to
+    every token row instead of a block representative, ReLU(x U) V, and the
+    result rounded to bf16 (to nearest even, from its float32 value) because it
+    feeds the bf16 score product of Eq. 1 - 2 with one head of width r.
+    Returns bf16 bits [N][r]."""
+    est = predictor_embeddings(x, u, v)
+    return bf16_round(est.astype(np.float32).astype(np.float64))
+
+
 # --------------------------------------------------------------------------
 # a5: layer threshold -> keep mask -> ascending kept-block list
 # --------------------------------------------------------------------------

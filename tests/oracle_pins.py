@@ -346,6 +346,54 @@ def _brute_predict(X, W, b, o):
     return M, M.sum(axis=0)
 
 
+def check_token_predictor(o) -> list:
+    """Per-token predictor embeddings: the hand example, agreement with the
+    block predictor on blocks of identical rows, exact doubling, and brute
+    force."""
+    out = []
+    e5 = golden()["E5_token_predictor"]
+    x = f2bits(e5["x"])
+    uq, vq, uk, vk = (f2bits(e5[n]) for n in ("u_q", "v_q", "u_k", "v_k"))
+    qt = o.token_embeddings(x, uq, vq)
+    kt = o.token_embeddings(x, uk, vk)
+    _fail(out, np.array_equal(o.bf16_decode(qt), np.array(e5["q_tok"])), f"E5 q_tok {o.bf16_decode(qt).tolist()}")
+    _fail(out, np.array_equal(o.bf16_decode(kt), np.array(e5["k_tok"])), f"E5 k_tok {o.bf16_decode(kt).tolist()}")
+    M, I = o.exact_block_scores(qt, kt, 1, 2, e5["block"], o.REDUCE_PAPER)
+    s2 = math.sqrt(2.0)
+    _fail(out, np.allclose(M * s2, np.array(e5["M_unscaled"]), rtol=1e-12, atol=1e-12), f"E5 M {M.tolist()}")
+    _fail(out, np.allclose(I * s2, np.array(e5["I_unscaled"]), rtol=1e-12, atol=1e-12), f"E5 I {I.tolist()}")
+    # a block whose rows are all equal has that row as its mean, so the token
+    # embedding of each row is the block predictor's output, rounded to bf16
+    rng = np.random.default_rng(11)
+    d, r, b, nb = 48, 16, 4, 5
+    base = torch_bf16_bits(rng.standard_normal((nb, d)).astype(np.float32))
+    xb = np.repeat(base, b, axis=0)
+    w = [torch_bf16_bits(rng.standard_normal(sh).astype(np.float32) / np.sqrt(sh[0])) for sh in ((d, r), (r, r))]
+    _, _, qh, _ = o.predict_scores(xb, w[0], w[1], w[0], w[1], b)
+    tok = o.token_embeddings(xb, w[0], w[1])
+    ref = torch_bf16_bits(np.repeat(qh, b, axis=0).astype(np.float32))
+    _fail(out, np.array_equal(tok, ref), "token embeddings disagree with the block predictor on constant blocks")
+    # X -> 2X doubles every embedding exactly (all rounding points scale by 2)
+    xr = torch_bf16_bits(rng.standard_normal((24, d)).astype(np.float32))
+    x2 = torch_bf16_bits(2.0 * o.bf16_decode(xr).astype(np.float32))
+    t1 = o.bf16_decode(o.token_embeddings(xr, w[0], w[1]))
+    t2 = o.bf16_decode(o.token_embeddings(x2, w[0], w[1]))
+    _fail(out, np.array_equal(t2, 2.0 * t1), "X -> 2X does not double the token embeddings")
+    # brute force: scalar loops, bf16 rounding through torch's conversion
+    X = o.bf16_decode(xr[:6, :8])
+    U = o.bf16_decode(w[0][:8, :4])
+    V = o.bf16_decode(w[1][:4, :4])
+
+    def bf(v):
+        return float(torch.tensor(float(v), dtype=torch.float32).to(torch.bfloat16).float())
+
+    brute = np.array([[bf(np.float32(sum(bf(np.float32(max(0.0, sum(X[i][c] * U[c][t] for c in range(8)))))
+                                         * V[t][v] for t in range(4)))) for v in range(4)] for i in range(6)])
+    got = o.bf16_decode(o.token_embeddings(xr[:6, :8], w[0][:8, :4], w[1][:4, :4]))
+    _fail(out, np.array_equal(got, brute), "token embeddings brute force")
+    return out
+
+
 # --------------------------------------------------------------------------
 def check_select(o) -> list:
     out = []
@@ -444,5 +492,5 @@ def check_movement(o) -> list:
 
 
 ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
-              check_exact_closed_form, check_exact_invariants, check_predictor, check_select,
-              check_movement]
+              check_exact_closed_form, check_exact_invariants, check_predictor, check_token_predictor,
+              check_select, check_movement]

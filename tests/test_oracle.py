@@ -42,6 +42,10 @@ MUTATIONS = [
      "hid = bf16_decode(xbar) @ bf16_decode(u)", [P.check_predictor]),
     ("predictor_transposed_v", "return bf16_decode(hid_bf16) @ bf16_decode(v)",
      "return bf16_decode(hid_bf16) @ bf16_decode(v).T", [P.check_predictor]),
+    ("token_no_final_round", "return bf16_round(est.astype(np.float32).astype(np.float64))",
+     "return bf16_round(np.trunc(est * 64) / 64)", [P.check_token_predictor]),
+    ("token_uses_transposed_u", "est = predictor_embeddings(x, u, v)", "est = predictor_embeddings(x, u.T, v)",
+     [P.check_token_predictor]),
     ("threshold_strict", "keep = s >= theta\n    elif mode == SELECT_MEAN", "keep = s > theta\n    elif mode == SELECT_MEAN",
      [P.check_select]),
     ("topk_ties_high_index", "-float(s[c]) if not np.isnan(s[c]) else 0.0, c))",
