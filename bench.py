@@ -229,6 +229,7 @@ def main():
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
     }
+    out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -242,6 +243,35 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, w)
     print(json.dumps(out), flush=True)
+
+
+def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):
+    """The per-token predictor variant on the same layer: embeddings of every
+    token (lemo_token_embeddings) scored by the exact-score kernel as one head
+    of width r.  Mean event times over `reps` calls after 3 warm-up calls."""
+    import torch
+    from contextual_token_sparsity_amd import lemo
+    nb = N // b
+    q_hat = torch.empty((N, r), dtype=torch.int16, device=dev)
+    k_hat = torch.empty((N, r), dtype=torch.int16, device=dev)
+    ws = torch.empty(lemo.lemo_token_embeddings_workspace(N, d, r), dtype=torch.uint8, device=dev)
+    I = torch.empty(nb, dtype=torch.float32, device=dev)
+    ws_s = torch.empty(lemo.lemo_block_scores_workspace(N, b), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 3)]
+    for i in range(reps + 3):
+        ev[i][0].record(stream)
+        lemo.lemo_token_embeddings(x, uq, vq, uk, vk, q_hat=q_hat, k_hat=k_hat, workspace=ws)
+        ev[i][1].record(stream)
+        lemo.lemo_block_scores(q_hat, k_hat, 1, r, b, lemo.REDUCE_PAPER, scores=I, workspace=ws_s)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_e = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[3:]]))
+    t_s = float(np.mean([e[1].elapsed_time(e[2]) for e in ev[3:]]))
+    f_e = 2.0 * N * d * 2 * r + 2.0 * 2 * N * r * r
+    f_s = 2.0 * N * N * r
+    return {"embeddings_ms": t_e, "scores_ms": t_s,
+            "embeddings_TFLOPs": f_e / (t_e * 1e-3) / 1e12, "scores_TFLOPs": f_s / (t_s * 1e-3) / 1e12,
+            "tokens_per_s": N / ((t_e + t_s) * 1e-3)}
 
 
 def movement_cold(gx, ga, sc, stream, dev, reps=5):

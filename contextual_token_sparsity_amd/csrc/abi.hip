@@ -128,6 +128,35 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
                        "lemo_predict_scores launch");
 }
 
+size_t lemo_token_embeddings_workspace(int n_tokens, int d_model, int rank) {
+  if (n_tokens <= 0 || d_model <= 0 || rank <= 0) return 0;
+  return lemo_token_ws_bytes(n_tokens, d_model, rank);
+}
+
+lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, const lemo_bf16* u_q,
+                                  const lemo_bf16* v_q, const lemo_bf16* u_k, const lemo_bf16* v_k, int rank,
+                                  lemo_bf16* q_hat, lemo_bf16* k_hat, int ld_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  REQUIRE(u_q && v_q && u_k && v_k, LEMO_ERR_INVALID_ARG, "a predictor matrix is NULL");
+  REQUIRE(n_tokens > 0 && d_model > 0 && rank > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d d_model=%d rank=%d)", n_tokens, d_model, rank);
+  REQUIRE(d_model % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_model %d (multiple of 64 supported)", d_model);
+  REQUIRE(rank % 64 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 64, at most 256)", rank);
+  lemo_status st;
+  if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
+  if ((st = check_rows(q_hat, ld_out, rank, "q_hat")) != LEMO_OK) return st;
+  if ((st = check_rows(k_hat, ld_out, rank, "k_hat")) != LEMO_OK) return st;
+  REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
+          "predictor matrices must be 16-byte aligned");
+  const size_t need = lemo_token_ws_bytes(n_tokens, d_model, rank);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned16(workspace), LEMO_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  return device_status(lemo_launch_token_embed(x, n_tokens, d_model, ld_x, u_q, v_q, u_k, v_k, rank, q_hat, k_hat,
+                                               ld_out, workspace, static_cast<hipStream_t>(stream)),
+                       "lemo_token_embeddings launch");
+}
+
 lemo_status lemo_select_mask(const float* scores, int n_blocks, int mode, float threshold, int keep_blocks,
                              uint8_t* mask, int32_t* kept_blocks, int32_t* n_kept, float* threshold_used,
                              int32_t* dev_status, void* stream) {

@@ -48,6 +48,12 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
                                const uint16_t* v_k, int rank, float* m_out, float* scores,
                                void* workspace, hipStream_t stream);
 
+size_t lemo_token_ws_bytes(int n_tokens, int d_model, int rank);
+hipError_t lemo_launch_token_embed(const uint16_t* x, int n_tokens, int d_model, int ld_x, const uint16_t* u_q,
+                                   const uint16_t* v_q, const uint16_t* u_k, const uint16_t* v_k, int rank,
+                                   uint16_t* q_hat, uint16_t* k_hat, int ld_out, void* workspace,
+                                   hipStream_t stream);
+
 hipError_t lemo_launch_select(const float* scores, int n_blocks, int mode, float threshold,
                               int keep_blocks, uint8_t* mask, int32_t* kept, int32_t* n_kept,
                               float* threshold_used, int32_t* dev_status, hipStream_t stream);

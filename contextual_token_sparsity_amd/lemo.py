@@ -28,6 +28,8 @@ _SIGS = {
     "lemo_block_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "lemo_predict_scores_workspace": (_sz, [_i, _i, _i, _i]),
     "lemo_predict_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lemo_token_embeddings_workspace": (_sz, [_i, _i, _i]),
+    "lemo_token_embeddings": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "lemo_select_mask": (_i, [_vp, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
@@ -142,6 +144,35 @@ def lemo_predict_scores(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, 
                                    _stream(x.device))
     _check(st, "lemo_predict_scores")
     return scores, block_scores
+
+
+def lemo_token_embeddings_workspace(n_tokens: int, d_model: int, rank: int) -> int:
+    return lib().lemo_token_embeddings_workspace(n_tokens, d_model, rank)
+
+
+def lemo_token_embeddings(x, u_q, v_q, u_k, v_k, d_model: int = None, q_hat=None, k_hat=None, workspace=None):
+    """Per-token predictor embeddings.  Returns (q_hat, k_hat), bf16 bits [N][rank]
+    as int16 tensors (the query and key of one head of width rank)."""
+    for t in (x, u_q, v_q, u_k, v_k):
+        _bf16(t)
+    n = x.shape[0]
+    d = x.shape[1] if d_model is None else d_model
+    rank = u_q.shape[1]
+    if q_hat is None:
+        q_hat = torch.empty((n, rank), dtype=torch.int16, device=x.device)
+    if k_hat is None:
+        k_hat = torch.empty((n, rank), dtype=torch.int16, device=x.device)
+    _bf16(q_hat), _bf16(k_hat)
+    if _ld(q_hat) != _ld(k_hat):
+        raise ValueError("q_hat and k_hat must share a row stride")
+    if workspace is None:
+        workspace = torch.empty(max(lemo_token_embeddings_workspace(n, d, rank), 1), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().lemo_token_embeddings(_ptr(x), n, d, _ld(x), _ptr(u_q), _ptr(v_q), _ptr(u_k), _ptr(v_k), rank,
+                                     _ptr(q_hat), _ptr(k_hat), _ld(q_hat), _ptr(workspace), workspace.numel(),
+                                     _stream(x.device))
+    _check(st, "lemo_token_embeddings")
+    return q_hat, k_hat
 
 
 def lemo_select_mask(scores, mode: int, threshold: float = 0.0, keep_blocks: int = 0, mask=None, kept_blocks=None,

@@ -5,6 +5,7 @@
  * moves only those rows:
  *   exact block scores   lemo_block_scores      (pages: Eq. 1, Eq. 2, Figure 6)
  *   predicted scores     lemo_predict_scores    (pages: Eq. 3, Figure 8)
+ *   per-token predictor  lemo_token_embeddings  (pages: Figure 8; scored by lemo_block_scores)
  *   threshold / compact  lemo_select_mask       (pages: layer threshold, Alg. 1 step 1)
  *   selective load       lemo_gather_pad        (pages: permutation-free movement)
  *   in-place addition    lemo_scatter_residual  (pages: permutation-free movement)
@@ -134,6 +135,31 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
                                 const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
                                 const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token predictor embeddings (Jenga 4.2.2, Figure 8, and its complexity
+ * analysis, which prices the query and key predictors at one pass per token).
+ *
+ * For every token row x of X:
+ *   q_hat = bf16( bf16(ReLU(x U_q)) V_q ),   k_hat = bf16( bf16(ReLU(x U_k)) V_k ),
+ * fp32 accumulation, round to nearest even at both bf16 points.  q_hat and
+ * k_hat are the query and key of ONE head of width `rank`: passing them to
+ * lemo_block_scores(q_hat, k_hat, n_tokens, 1, rank, ld_out, ld_out, block,
+ * ...) gives the per-token predicted block scores (with that call's
+ * 1/sqrt(rank) scale; rank 64 or 128 there).
+ *
+ *  x             bf16 [n_tokens][ld_x], d_model columns used (d_model % 64 == 0).
+ *  u_q, u_k      bf16 [d_model][rank]; v_q, v_k bf16 [rank][rank] (rank % 64 == 0, <= 256).
+ *  q_hat, k_hat  bf16 [n_tokens][ld_out] outputs, rank columns written.
+ *  workspace     lemo_token_embeddings_workspace() bytes (transposed weights
+ *                and the [n_tokens][2 rank] hidden activations).
+ * Errors: INVALID_ARG, UNSUPPORTED (d_model, rank), ALIGNMENT, WORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t lemo_token_embeddings_workspace(int n_tokens, int d_model, int rank);
+lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model, int ld_x,
+                                  const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                  const lemo_bf16* v_k, int rank, lemo_bf16* q_hat, lemo_bf16* k_hat,
+                                  int ld_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Layer threshold and compaction (Jenga 4.2.1, "Layer-specific Threshold";

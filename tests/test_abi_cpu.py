@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
 
@@ -71,6 +71,28 @@ def ps(L, x=P, n=1024, d=512, ldx=512, b=64, r=64, M=NULL, I=P, ws=P, wsb=1 << 3
 ])
 def test_predict_rejects(L, kw, status):
     assert ps(L, **kw) == status
+
+
+def te(L, x=P, n=1024, d=512, ldx=512, uq=P, r=128, q=P, k=P, ldo=128, ws=P, wsb=1 << 30):
+    return L.lemo_token_embeddings(x, n, d, ldx, uq, P, P, P, r, q, k, ldo, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=NULL), INVALID), (dict(uq=NULL), INVALID), (dict(q=NULL), INVALID), (dict(k=NULL), INVALID),
+    (dict(n=0), INVALID), (dict(r=0), INVALID), (dict(ldx=256), INVALID), (dict(ldo=64), INVALID),
+    (dict(d=100, ldx=104), UNSUP), (dict(r=96, ldo=96), UNSUP), (dict(r=320, ldo=320), UNSUP),
+    (dict(x=P2), ALIGN), (dict(uq=P2), ALIGN), (dict(q=P2), ALIGN), (dict(ldo=132), ALIGN),
+    (dict(ws=NULL), WS), (dict(wsb=1000), WS),
+])
+def test_token_embeddings_rejects(L, kw, status):
+    assert te(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def test_token_embeddings_workspace(L):
+    # [U_q | U_k]^T + V_q^T, V_k^T + hidden [N][2r], each 256-byte aligned
+    assert L.lemo_token_embeddings_workspace(16384, 4096, 128) == 256 * 4096 * 2 + 2 * 128 * 128 * 2 + 16384 * 256 * 2
+    assert L.lemo_token_embeddings_workspace(0, 4096, 128) == 0
 
 
 def sel(L, s=P, nb=256, mode=1, th=0.0, k=10, mask=P, kept=P, nk=P):

@@ -511,3 +511,98 @@ def test_scatter_every_bf16_pair():
         bad += ((res != ref.view(torch.int16)) & ~both_nan).sum()
     torch.cuda.synchronize()
     assert int(bad.item()) == 0
+
+
+# ------------------------------------------------- per-token predictor
+def _embeddings_close(got_bits, ref_bits):
+    """Both sides round the hidden layer and the output to bf16 from fp32
+    values summed in different orders, so an element may land one bf16 step
+    away where a value sits near a rounding tie.  Accept: at least 99% of the
+    elements bit-identical, every element within 2^-7 of (|ref| + mean |ref|)."""
+    got = O.bf16_decode(got_bits)
+    ref = O.bf16_decode(ref_bits)
+    same = float(np.mean(got_bits == ref_bits))
+    tol = 2.0 ** -7 * (np.abs(ref) + np.abs(ref).mean())
+    return same >= 0.99 and bool(np.all(np.abs(got - ref) <= tol)), same
+
+
+TOKEN_SMALL = [
+    # (N, d, r)
+    (256, 128, 64),
+    (320, 192, 128),      # N not a multiple of the 128-row tile
+    (200, 256, 256),      # rank 256: two column tiles per product
+    (64, 64, 64),         # a single partial tile
+]
+
+
+@pytest.mark.parametrize("shape", TOKEN_SMALL, ids=lambda s: "N%d_d%d_r%d" % s)
+def test_token_embeddings_small(shape):
+    n, d, r = shape
+    say("token embeddings", shape)
+    x, w = _pred_inputs(n * 7 + d + r, n, d, r)
+    ref_q = O.token_embeddings(x, w[0], w[1])
+    ref_k = O.token_embeddings(x, w[2], w[3])
+    qd, kd = lemo.lemo_token_embeddings(dev(x), *[dev(a) for a in w])
+    ok, same = _embeddings_close(host_bits(qd), ref_q)
+    assert ok, same
+    ok, same = _embeddings_close(host_bits(kd), ref_k)
+    assert ok, same
+
+
+def test_token_embeddings_strided():
+    n, d, r = 384, 128, 64
+    x, w = _pred_inputs(17, n, d, r)
+    xp = padded(x, 200, 0x7FC0)
+    out = padded(np.zeros((n, r), np.uint16), 72, 0x1234)
+    out2 = padded(np.zeros((n, r), np.uint16), 72, 0x1234)
+    lemo.lemo_token_embeddings(xp[:, :d], *[dev(a) for a in w], q_hat=out[:, :r], k_hat=out2[:, :r])
+    ok, _ = _embeddings_close(host_bits(out)[:, :r], O.token_embeddings(x, w[0], w[1]))
+    assert ok
+    assert np.all(host_bits(out)[:, r:] == 0x1234) and np.all(host_bits(out2)[:, r:] == 0x1234)
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+def test_token_predictor_scores_small(mode):
+    """Per-token embeddings -> exact-score kernel with one head of width r,
+    against the oracle's scores of the oracle's embeddings."""
+    n, d, r, b = 1024, 256, 128, 64
+    x, w = _pred_inputs(5, n, d, r)
+    rq, rk = O.token_embeddings(x, w[0], w[1]), O.token_embeddings(x, w[2], w[3])
+    M_ref, I_ref = O.exact_block_scores(rq, rk, 1, r, b, mode)
+    qd, kd = lemo.lemo_token_embeddings(dev(x), *[dev(a) for a in w])
+    M = torch.empty((n // b, n // b), device="cuda")
+    I, _ = lemo.lemo_block_scores(qd, kd, 1, r, b, mode, block_scores=M)
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok, worst
+    ok, worst = scores_close(M.cpu().numpy(), M_ref)
+    assert ok, worst
+
+
+def test_token_predictor_full_size():
+    """Llama2-7B shape (N=16384, d=4096, r=128): embeddings against the
+    oracle's everywhere, block scores on sampled key-block columns."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("token predictor full size")
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, rank=w.rank, planted_frac=w.planted_frac,
+                         with_y=False)
+    rq = O.token_embeddings(L.x, L.u_q, L.v_q)
+    rk = O.token_embeddings(L.x, L.u_k, L.v_k)
+    qd, kd = lemo.lemo_token_embeddings(dev(L.x), dev(L.u_q), dev(L.v_q), dev(L.u_k), dev(L.v_k))
+    ok, same = _embeddings_close(host_bits(qd), rq)
+    assert ok, same
+    ok, same = _embeddings_close(host_bits(kd), rk)
+    assert ok, same
+    I, _ = lemo.lemo_block_scores(qd, kd, 1, w.rank, w.block, O.REDUCE_PAPER)
+    Ig = I.cpu().numpy()
+    nb = w.n_blocks
+    for c in (0, 1, nb // 3, nb - 1):
+        ref, _ = O.exact_column_score(rq, rk, 1, w.rank, w.block, O.REDUCE_PAPER, c)
+        assert abs(Ig[c] - ref) <= 1e-2 * abs(ref), (c, Ig[c], ref)
+
+
+def test_token_embeddings_deterministic():
+    n, d, r = 512, 256, 128
+    x, w = _pred_inputs(23, n, d, r)
+    a = lemo.lemo_token_embeddings(dev(x), *[dev(t) for t in w])
+    b = lemo.lemo_token_embeddings(dev(x), *[dev(t) for t in w])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
