@@ -292,6 +292,45 @@ def gather_pad(src, block: int, kept, n_kept: int, dst_init, pad_multiple: int):
     return dst, n_pad > cap
 
 
+def linear_bf16(a, weight) -> np.ndarray:
+    """A layer's linear map on bf16 rows: a weightᵀ with weight stored
+    [out][in] (the usual Linear layout), the real product rounded to bf16
+    from its float32 value.  Returns bf16 bits [rows][out]."""
+    prod = bf16_decode(a) @ bf16_decode(weight).T
+    return bf16_round(prod.astype(np.float32).astype(np.float64))
+
+
+def gather_linear(x, block: int, kept, n_kept: int, weight, dst_init, pad_multiple: int):
+    """Selective load fused into the layer's first product ([Jenga] 4.2.3:
+    the kept tokens are read from their original rows inside the computation,
+    Figure 18).  Reading: the same rows, order and zero padding as
+    `gather_pad`, each row multiplied by weightᵀ and rounded to bf16; rows of
+    dst past the padding keep their contents, rows past its capacity are
+    dropped and reported.  Returns (dst bits, overflowed)."""
+    dst = np.array(dst_init, dtype=np.uint16, copy=True)
+    cap = dst.shape[0]
+    rows = kept_token_rows(kept, n_kept, block)
+    n_rows = rows.size
+    n_pad = -(-n_rows // pad_multiple) * pad_multiple
+    take = min(n_rows, cap)
+    width = np.asarray(weight).shape[0]
+    if take:
+        dst[:take, :width] = linear_bf16(np.asarray(x)[rows[:take]], weight)
+    for p in range(n_rows, min(n_pad, cap)):
+        dst[p, :width] = 0
+    return dst, n_pad > cap
+
+
+def linear_scatter(a, weight, residual, block: int, kept, n_kept: int):
+    """In-place addition fused into the layer's last product ([Jenga] 4.2.3,
+    Figure 18).  Reading: row p of a (the dense kept rows) times weightᵀ,
+    rounded to bf16, then added to the original row of kept token p exactly as
+    `scatter_residual` adds it.  Returns new residual bits."""
+    rows = kept_token_rows(kept, n_kept, block)
+    y = linear_bf16(np.asarray(a)[:rows.size], weight) if rows.size else np.zeros((0, 0), np.uint16)
+    return scatter_residual(residual, block, kept, n_kept, y)
+
+
 def scatter_residual(residual, block: int, kept, n_kept: int, y):
     """In-place addition ([Jenga] 4.2.3): the layer output of each kept token
     (row p of y, in kept-block order) is added to that token's original row of

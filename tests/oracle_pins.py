@@ -394,6 +394,52 @@ def check_token_predictor(o) -> list:
     return out
 
 
+def check_fused_movement(o) -> list:
+    """Selective load fused into a product and in-place addition fused into a
+    product: the hand example, the identity weight reducing them to the plain
+    gather and scatter, and brute force of the product's rounding."""
+    out = []
+    e6 = golden()["E6_fused_movement"]
+    x = f2bits(e6["x"])
+    w = f2bits(e6["weight"])
+    kept = np.array(e6["kept"], np.int32)
+    b, pad, cap = e6["block"], e6["pad_multiple"], e6["cap_rows"]
+    dst0 = np.full((cap, 2), 0x5A5A, np.uint16)
+    dst, over = o.gather_linear(x, b, kept, kept.size, w, dst0, pad)
+    rows = np.array(e6["gather_linear_rows"])
+    _fail(out, not over and np.array_equal(o.bf16_decode(dst[:4]), rows), f"E6 gathered product {dst[:4].tolist()}")
+    _fail(out, np.all(dst[4:8] == 0) and np.all(dst[8:] == 0x5A5A), "E6 padding / untouched rows")
+    res = o.linear_scatter(f2bits(e6["a"]), w, x, b, kept, kept.size)
+    _fail(out, np.array_equal(o.bf16_decode(res), np.array(e6["residual_after"])), f"E6 residual {o.bf16_decode(res).tolist()}")
+    # the identity weight reduces both to the plain movement, bit for bit
+    rng = np.random.default_rng(13)
+    n, d, blk = 96, 24, 8
+    xr = torch_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    eye = f2bits(np.eye(d))
+    kp = np.array([1, 4, 5, 9], np.int32)
+    init = np.full((48, d), 0x1357, np.uint16)
+    g1, o1 = o.gather_linear(xr, blk, kp, kp.size, eye, init, 16)
+    g2, o2 = o.gather_pad(xr, blk, kp, kp.size, init, 16)
+    _fail(out, np.array_equal(g1, g2) and o1 == o2, "identity weight: gather_linear != gather_pad")
+    ar = torch_bf16_bits(rng.standard_normal((kp.size * blk, d)).astype(np.float32))
+    s1 = o.linear_scatter(ar, eye, xr, blk, kp, kp.size)
+    s2 = o.scatter_residual(xr, blk, kp, kp.size, ar)
+    _fail(out, np.array_equal(s1, s2), "identity weight: linear_scatter != scatter_residual")
+    # rows of dropped blocks are untouched
+    dropped = np.setdiff1d(np.arange(n // blk), kp)
+    drows = (dropped[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+    _fail(out, np.array_equal(s1[drows], xr[drows]), "linear_scatter touched a dropped row")
+    # brute force of the product's rounding on a tiny case
+    A = torch_bf16_bits(rng.standard_normal((5, 7)).astype(np.float32))
+    W = torch_bf16_bits(rng.standard_normal((3, 7)).astype(np.float32))
+    Ad, Wd = o.bf16_decode(A), o.bf16_decode(W)
+    brute = np.array([[float(torch.tensor(float(np.float32(sum(Ad[i][k] * Wd[j][k] for k in range(7)))),
+                                          dtype=torch.float32).to(torch.bfloat16).float()) for j in range(3)]
+                      for i in range(5)])
+    _fail(out, np.array_equal(o.bf16_decode(o.linear_bf16(A, W)), brute), "linear_bf16 brute force")
+    return out
+
+
 # --------------------------------------------------------------------------
 def check_select(o) -> list:
     out = []
@@ -493,4 +539,4 @@ def check_movement(o) -> list:
 
 ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
               check_exact_closed_form, check_exact_invariants, check_predictor, check_token_predictor,
-              check_select, check_movement]
+              check_select, check_movement, check_fused_movement]

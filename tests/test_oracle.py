@@ -46,6 +46,12 @@ MUTATIONS = [
      "return bf16_round(np.trunc(est * 64) / 64)", [P.check_token_predictor]),
     ("token_uses_transposed_u", "est = predictor_embeddings(x, u, v)", "est = predictor_embeddings(x, u.T, v)",
      [P.check_token_predictor]),
+    ("linear_weight_not_transposed", "prod = bf16_decode(a) @ bf16_decode(weight).T", "prod = bf16_decode(a) @ bf16_decode(weight)",
+     [P.check_fused_movement]),
+    ("gather_linear_dense_rows", "dst[:take, :width] = linear_bf16(np.asarray(x)[rows[:take]], weight)",
+     "dst[:take, :width] = linear_bf16(np.asarray(x)[:take], weight)", [P.check_fused_movement]),
+    ("gather_linear_no_pad", "        dst[p, :width] = 0\n    return dst, n_pad > cap\n\n\ndef linear_scatter",
+     "        pass\n    return dst, n_pad > cap\n\n\ndef linear_scatter", [P.check_fused_movement]),
     ("threshold_strict", "keep = s >= theta\n    elif mode == SELECT_MEAN", "keep = s > theta\n    elif mode == SELECT_MEAN",
      [P.check_select]),
     ("topk_ties_high_index", "-float(s[c]) if not np.isnan(s[c]) else 0.0, c))",
@@ -57,7 +63,8 @@ MUTATIONS = [
     ("round_no_subnormals", "qexp = np.maximum(e - 8, -133)", "qexp = e - 8", [P.check_bf16_round]),
     ("gather_wrong_block", "return (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)",
      "return ((kept[:, None] + 1) * block + np.arange(block)[None, :]).reshape(-1) % 6", [P.check_movement]),
-    ("pad_not_zeroed", "dst[p, :width] = 0", "pass", [P.check_movement]),
+    ("pad_not_zeroed", "        dst[p, :width] = 0\n    return dst, n_pad > cap\n\n\ndef linear_bf16",
+     "        pass\n    return dst, n_pad > cap\n\n\ndef linear_bf16", [P.check_movement]),
     ("scatter_into_dense_rows", "for p, t in enumerate(rows):", "for p, t in enumerate(range(rows.size)):",
      [P.check_movement]),
 ]
