@@ -205,4 +205,44 @@ lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, 
                        "lemo_scatter_residual launch");
 }
 
+lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int ld_x, int block,
+                               const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* weight,
+                               int d_out, int ld_w, lemo_bf16* y, int ld_y, int cap_rows, int pad_multiple,
+                               int32_t* dev_status, void* stream) {
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && d_in > 0 && d_out > 0 && cap_rows > 0 && pad_multiple > 0,
+          LEMO_ERR_INVALID_ARG, "sizes must be positive (n_tokens=%d block=%d d_in=%d d_out=%d cap_rows=%d pad=%d)",
+          n_tokens, block, d_in, d_out, cap_rows, pad_multiple);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
+  lemo_status st;
+  if ((st = check_rows(x, ld_x, d_in, "x")) != LEMO_OK) return st;
+  if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
+  if ((st = check_rows(y, ld_y, d_out, "y")) != LEMO_OK) return st;
+  return device_status(lemo_launch_gather_linear(x, n_tokens, d_in, ld_x, block, kept_blocks, n_kept, weight, d_out,
+                                                 ld_w, y, ld_y, cap_rows, pad_multiple, dev_status,
+                                                 static_cast<hipStream_t>(stream)),
+                       "lemo_gather_linear launch");
+}
+
+lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_rows, const lemo_bf16* weight,
+                                int d_out, int ld_w, lemo_bf16* residual, int n_tokens, int ld_res, int block,
+                                const int32_t* kept_blocks, const int32_t* n_kept, int32_t* dev_status,
+                                void* stream) {
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && d_in > 0 && d_out > 0 && cap_rows > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d d_in=%d d_out=%d cap_rows=%d)", n_tokens, block, d_in, d_out,
+          cap_rows);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
+  lemo_status st;
+  if ((st = check_rows(a, ld_a, d_in, "a")) != LEMO_OK) return st;
+  if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
+  if ((st = check_rows(residual, ld_res, d_out, "residual")) != LEMO_OK) return st;
+  return device_status(lemo_launch_linear_scatter(a, d_in, ld_a, cap_rows, weight, d_out, ld_w, residual, n_tokens,
+                                                  ld_res, block, kept_blocks, n_kept, dev_status,
+                                                  static_cast<hipStream_t>(stream)),
+                       "lemo_linear_scatter launch");
+}
+
 }  // extern "C"

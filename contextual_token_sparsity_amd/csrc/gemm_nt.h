@@ -1,0 +1,260 @@
+// C = A B^T on the matrix cores (gfx950), with A and B row-major in the
+// reduction index (like Q K^T; a Linear layer's weight [out][in] is such a B).
+// Device code shared by the per-token predictor and the fused movement
+// products; each translation unit gets its own copy (internal linkage).
+//
+// One 64 x 128 tile of C per workgroup of 4 waves (32 x 64 per wave as 1 x 2
+// v_mfma_f32_32x32x16_bf16 tiles).  The reduction streams in 64-wide chunks
+// through a 3-stage LDS ring filled by direct global->LDS loads (two chunks in
+// flight), with the 16-byte pieces of each 128-B LDS row XOR-swizzled so that
+// the operand reads are free of bank conflicts.  Workgroup ids go round-robin
+// over the 8 XCDs; the column tiles of one row block are given to ids on the
+// same XCD, back to back, so the second read of those rows of A hits L2.
+//
+// Epilogues (EPI):
+//   kEpiReluBf16   C[m][n] = bf16(max(0, acc))                       (dense rows)
+//   kEpiBf16       C[m][n] = bf16(acc)                               (dense rows)
+//   kEpiGather     A row m is token row tok(m) of the kept blocks (selective
+//                  load in the operand prologue); C[m][n] = bf16(acc) for
+//                  m < R, 0 for R <= m < roundup(R, pad), within cap rows
+//   kEpiScatterAdd A rows dense; the product is added in place to residual
+//                  row tok(m): res = bf16(f32(res) + f32(bf16(acc))), m < R
+// with tok(m) = kept[m / block] * block + m % block and R = n_kept * block
+// read on the device.  Rows whose kept index is out of range are skipped and
+// flagged, as the stand-alone gather and scatter do.
+#pragma once
+
+#include "lemo_internal.h"
+
+namespace {
+
+namespace gemm {
+
+constexpr int kTM = 64;                             // tile rows (A)
+constexpr int kTN = 128;                            // tile columns (B rows)
+constexpr int kWaves = 4;                           // 2 x 2 waves of 32 x 64
+constexpr int kThreads = kWaves * 64;
+constexpr int kChunk = 64;                          // reduction elements per stage
+constexpr int kRowBytes = kChunk * 2;               // 128 B
+constexpr int kRegionA = kTM * kRowBytes;           // 8 KiB
+constexpr int kRegionB = kTN * kRowBytes;           // 16 KiB
+constexpr int kStageBytes = kRegionA + kRegionB;
+constexpr int kDmaA = kRegionA / (kThreads * 16);   // 2 loads of 16 B per thread
+constexpr int kDmaB = kRegionB / (kThreads * 16);   // 4
+constexpr int kStages = 3;                          // 72 KiB: two workgroups per CU
+constexpr int kDmaPerChunk = kDmaA + kDmaB;
+
+enum { kEpiReluBf16 = 0, kEpiBf16 = 1, kEpiGather = 2, kEpiScatterAdd = 3 };
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_tile[kStages * kStageBytes];
+
+// Piece swizzle of LDS row r (distinct for 8 consecutive rows and for the 8
+// even/odd rows among 16 consecutive rows).
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+__device__ __forceinline__ int acc_row(int lane, int e) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+
+// 16-byte direct global->LDS load per lane: lane l reads base + voff and writes lds + 16 l.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+// Operands of up to two independent products launched together (blockIdx.z).
+struct Args {
+  const uint16_t* a[2];
+  const uint16_t* b[2];
+  uint16_t* c[2];
+};
+
+// Kept-block row map of the gather / scatter epilogues.
+struct RowMap {
+  const int32_t* kept;
+  const int32_t* n_kept;
+  int block;
+  int n_tokens;
+  int pad_multiple;
+  int32_t* status;
+};
+
+// C[m][n] = sum_k A[m][k] B[n][k] for m < M (the row capacity of C for the
+// gather epilogue), n < Nn; K a multiple of 64.  Rows of A (B) past the rows
+// in use read a valid row, and their results are dropped.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ldb, int M, int Nn, int K, int ldc,
+                                                         int tm_count, int tn_count, RowMap rm) {
+  constexpr bool kMapped = EPI == kEpiGather || EPI == kEpiScatterAdd;
+  const uint16_t* __restrict__ A = g.a[blockIdx.z];
+  const uint16_t* __restrict__ B = g.b[blockIdx.z];
+  uint16_t* __restrict__ C = g.c[blockIdx.z];
+  int tm, tn;
+  {
+    const int w = blockIdx.x;
+    if (tm_count % 8 == 0) {
+      const int j = w / 8;
+      tn = j % tn_count;
+      tm = (j / tn_count) * 8 + w % 8;
+    } else {
+      tm = w / tn_count;
+      tn = w % tn_count;
+    }
+  }
+  const int m0 = tm * kTM, n0 = tn * kTN;
+
+  // rows in use: all M, or the kept rows (plus zero padding for the gather)
+  int R = M, rows_used = M, nb = 0;
+  if (kMapped) {
+    nb = rm.n_tokens / rm.block;
+    const int nk = *rm.n_kept;
+    const bool bad = nk < 0 || nk > nb;
+    R = bad ? 0 : nk * rm.block;
+    if (EPI == kEpiGather) {
+      const long long pad = ((long long)R + rm.pad_multiple - 1) / rm.pad_multiple * rm.pad_multiple;
+      rows_used = (int)min((long long)M, pad);
+      if (rm.status && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        int f = 0;
+        if (bad) f |= LEMO_DEV_BAD_KEPT;
+        if (pad > M) f |= LEMO_DEV_CAP_OVERFLOW;
+        if (f) atomicOr(rm.status, f);
+      }
+      R = min(R, M);
+    } else {
+      if (rm.status && bad && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+        atomicOr(rm.status, LEMO_DEV_BAD_KEPT);
+      if (R > M) {
+        if (rm.status && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+          atomicOr(rm.status, LEMO_DEV_CAP_OVERFLOW);
+        R = M;
+      }
+      rows_used = R;
+    }
+  }
+  if (m0 >= rows_used) return;   // the whole workgroup: before any barrier
+
+  // token row of kept row m, or -1 (index out of range)
+  auto tok_of = [&](int m) {
+    const int blk = rm.kept[m / rm.block];
+    return (blk >= 0 && blk < nb) ? blk * rm.block + m % rm.block : -1;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave >> 1, wk = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)g_tile;
+
+  // instruction i of wave w fills LDS row (i*4 + w)*8 + lane/8 of a region,
+  // physical piece lane%8, which holds logical piece (lane%8) ^ swz(row)
+  uint32_t voffA[kDmaA], voffB[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(r);
+    if (i < kDmaA) {
+      int arow;
+      if (EPI == kEpiGather) {
+        const int t = m0 + r < R ? tok_of(m0 + r) : -1;
+        arow = t >= 0 ? t : 0;
+      } else {
+        arow = min(m0 + r, rows_used - 1);
+      }
+      voffA[i] = (uint32_t)(((size_t)arow * lda + piece * 8) * 2);
+    }
+    voffB[i] = (uint32_t)(((size_t)min(n0 + r, Nn - 1) * ldb + piece * 8) * 2);
+  }
+  auto issue = [&](int c, int stage) {
+    const uint32_t base = lds0 + (uint32_t)(stage * kStageBytes);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+      if (i < kDmaA) dma16(A + c * kChunk, voffA[i], base + (uint32_t)((i * kWaves + wave) * 1024));
+      dma16(B + c * kChunk, voffB[i], base + kRegionA + (uint32_t)((i * kWaves + wave) * 1024));
+    }
+  };
+
+  // per-lane LDS read offsets for the 4 k-steps of a chunk (operand rows all
+  // have r & 15 == l32 & 15, so one swizzle serves them)
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int piece = (2 * s + hi) ^ swz(l32);
+    offA[s] = (uint32_t)((wq * 32 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(kRegionA + (wk * 64 + l32) * kRowBytes + piece * 16);
+  }
+
+  lemo_f32x16 acc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
+  lemo_bf16x8 fa[2], fb[2][2];
+  auto read_frags = [&](int buf, const uint8_t* st, int s) {
+    fa[buf] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
+  };
+
+  const int nchunks = K / kChunk;
+  issue(0, 0);
+  if (nchunks > 1) issue(1, 1);
+  for (int c = 0; c < nchunks; ++c) {
+    // this wave's loads of chunk c have landed (only chunk c+1's may still be
+    // in flight); after the barrier every wave's have, and every wave is done
+    // with chunk c-1's stage, which is refilled with chunk c+2
+    if (c + 1 < nchunks)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kDmaPerChunk) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 2 < nchunks) issue(c + 2, (c + 2) % kStages);
+    const uint8_t* st = g_tile + (c % kStages) * kStageBytes;
+    read_frags(0, st, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < 4) read_frags(cur ^ 1, st, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur], fb[cur][b], acc[b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // epilogue, bounds-checked
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = m0 + wq * 32 + acc_row(lane, e);
+    if (row >= rows_used) continue;
+    int t = row;
+    if (kMapped && row < R) t = tok_of(row);
+    if (kMapped && row < R && t < 0) {
+      if (rm.status) atomicOr(rm.status, LEMO_DEV_BAD_KEPT);
+      continue;
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = n0 + wk * 64 + b * 32 + l32;
+      if (col >= Nn) continue;
+      float v = acc[b][e];
+      if (EPI == kEpiReluBf16) v = fmaxf(v, 0.f);
+      if (EPI == kEpiScatterAdd) {
+        uint16_t* p = C + (size_t)t * ldc + col;
+        const float y = lemo_bf16_to_f32(lemo_f32_to_bf16(v));
+        *p = (uint16_t)lemo_f32_to_bf16(lemo_bf16_to_f32(*p) + y);
+      } else if (EPI == kEpiGather && row >= R) {
+        C[(size_t)row * ldc + col] = 0;   // zero padding
+      } else {
+        C[(size_t)row * ldc + col] = (uint16_t)lemo_f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+// Grid of k_gemm_nt: row tiles x column tiles, products in z.
+inline dim3 grid_for(int rows, int cols, int products, int& tm_count, int& tn_count) {
+  tm_count = (rows + kTM - 1) / kTM;
+  tn_count = (cols + kTN - 1) / kTN;
+  return dim3(tm_count * tn_count, 1, products);
+}
+
+}  // namespace gemm
+
+}  // namespace

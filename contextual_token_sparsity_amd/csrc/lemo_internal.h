@@ -54,6 +54,15 @@ hipError_t lemo_launch_token_embed(const uint16_t* x, int n_tokens, int d_model,
                                    uint16_t* q_hat, uint16_t* k_hat, int ld_out, void* workspace,
                                    hipStream_t stream);
 
+hipError_t lemo_launch_gather_linear(const uint16_t* x, int n_tokens, int d_in, int ld_x, int block,
+                                     const int32_t* kept, const int32_t* n_kept, const uint16_t* w, int d_out,
+                                     int ld_w, uint16_t* y, int ld_y, int cap_rows, int pad_multiple,
+                                     int32_t* dev_status, hipStream_t stream);
+hipError_t lemo_launch_linear_scatter(const uint16_t* a, int d_in, int ld_a, int cap_rows, const uint16_t* w,
+                                      int d_out, int ld_w, uint16_t* res, int n_tokens, int ld_res, int block,
+                                      const int32_t* kept, const int32_t* n_kept, int32_t* dev_status,
+                                      hipStream_t stream);
+
 hipError_t lemo_launch_select(const float* scores, int n_blocks, int mode, float threshold,
                               int keep_blocks, uint8_t* mask, int32_t* kept, int32_t* n_kept,
                               float* threshold_used, int32_t* dev_status, hipStream_t stream);

@@ -33,6 +33,8 @@ _SIGS = {
     "lemo_select_mask": (_i, [_vp, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_gather_linear": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp]),
+    "lemo_linear_scatter": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "lemo_status_string": (ctypes.c_char_p, [_i]),
     "lemo_last_error": (ctypes.c_char_p, []),
     "lemo_version": (_i, []),
@@ -212,6 +214,30 @@ def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: i
     st = lib().lemo_scatter_residual(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
                                      _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
     _check(st, "lemo_scatter_residual")
+    return residual
+
+
+def lemo_gather_linear(x, block: int, kept_blocks, n_kept, weight, y, pad_multiple: int = 1, d_in: int = None,
+                       n_tokens: int = None, dev_status=None):
+    """Selective load fused into a product: y[p] = bf16(x[token(p)] weightᵀ), zero-padded."""
+    _bf16(x), _bf16(weight), _bf16(y)
+    din = x.shape[1] if d_in is None else d_in
+    n = x.shape[0] if n_tokens is None else n_tokens
+    st = lib().lemo_gather_linear(_ptr(x), n, din, _ld(x), block, _ptr(kept_blocks), _ptr(n_kept), _ptr(weight),
+                                  weight.shape[0], _ld(weight), _ptr(y), _ld(y), y.shape[0], pad_multiple,
+                                  _ptr(dev_status), _stream(x.device))
+    _check(st, "lemo_gather_linear")
+    return y
+
+
+def lemo_linear_scatter(a, weight, residual, block: int, kept_blocks, n_kept, d_in: int = None, dev_status=None):
+    """In-place addition fused into a product: residual[token(p)] += bf16(a[p] weightᵀ)."""
+    _bf16(a), _bf16(weight), _bf16(residual)
+    din = a.shape[1] if d_in is None else d_in
+    st = lib().lemo_linear_scatter(_ptr(a), din, _ld(a), a.shape[0], _ptr(weight), weight.shape[0], _ld(weight),
+                                   _ptr(residual), residual.shape[0], _ld(residual), block, _ptr(kept_blocks),
+                                   _ptr(n_kept), _ptr(dev_status), _stream(a.device))
+    _check(st, "lemo_linear_scatter")
     return residual
 
 

@@ -9,6 +9,7 @@
  *   threshold / compact  lemo_select_mask       (pages: layer threshold, Alg. 1 step 1)
  *   selective load       lemo_gather_pad        (pages: permutation-free movement)
  *   in-place addition    lemo_scatter_residual  (pages: permutation-free movement)
+ *   movement fused into the layer's products: lemo_gather_linear, lemo_linear_scatter
  * "The pages" are "Jenga: Enhancing LLM Long-Context Fine-tuning with
  * Contextual Token Sparsity" (USENIX ATC'25; summary page, section 4.2) and
  * the review page of its arXiv version "LeMo" (2501.09767).
@@ -200,6 +201,38 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
                             const int32_t* kept_blocks, const int32_t* n_kept, lemo_bf16* dst,
                             int ld_dst, int cap_rows, int pad_multiple, int32_t* dev_status,
                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token movement fused into the layer's products (Jenga 4.2.3, permutation-
+ * free token movement, Figure 18: selective load and in-place addition are
+ * carried out inside the computation, not as separate passes).
+ *
+ * weight is a Linear layer's bf16 matrix stored [d_out][ld_w] (out x in,
+ * d_in columns used); the product of a row r is r weight^T with fp32
+ * accumulation, rounded to nearest even to bf16.  tok(p) and R = n_kept *
+ * block are as for lemo_gather_pad; n_kept and kept_blocks are read on the
+ * device.  The results are bit for bit those of lemo_gather_pad followed by
+ * the product, and of the product followed by lemo_scatter_residual.
+ *
+ * lemo_gather_linear: y[p] = bf16(x[tok(p)] weight^T) for p < R; rows R ..
+ *   roundup(R, pad_multiple)-1 are zero; rows past that are untouched; rows
+ *   past cap_rows are dropped and flag LEMO_DEV_CAP_OVERFLOW.
+ *   x [n_tokens][ld_x] (d_in used), y [cap_rows][ld_y] (d_out used).
+ * lemo_linear_scatter: residual[tok(p)] = bf16(residual[tok(p)] +
+ *   bf16(a[p] weight^T)) for p < R, in place; other rows untouched.  a holds
+ *   the kept rows densely, [cap_rows][ld_a] (d_in used); kept rows past
+ *   cap_rows are skipped and flag LEMO_DEV_CAP_OVERFLOW.
+ * Invalid kept indices are skipped and flag LEMO_DEV_BAD_KEPT.
+ * d_in a multiple of 64.  Errors: INVALID_ARG, UNSUPPORTED (d_in), ALIGNMENT.
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int ld_x, int block,
+                               const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* weight,
+                               int d_out, int ld_w, lemo_bf16* y, int ld_y, int cap_rows, int pad_multiple,
+                               int32_t* dev_status, void* stream);
+lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_rows, const lemo_bf16* weight,
+                                int d_out, int ld_w, lemo_bf16* residual, int n_tokens, int ld_res, int block,
+                                const int32_t* kept_blocks, const int32_t* n_kept, int32_t* dev_status,
+                                void* stream);
 
 /* ------------------------------------------------------------------------
  * In-place addition (Jenga 4.2.3): the layer output of every kept token is

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
 
@@ -93,6 +93,37 @@ def test_token_embeddings_workspace(L):
     # [U_q | U_k]^T + V_q^T, V_k^T + hidden [N][2r], each 256-byte aligned
     assert L.lemo_token_embeddings_workspace(16384, 4096, 128) == 256 * 4096 * 2 + 2 * 128 * 128 * 2 + 16384 * 256 * 2
     assert L.lemo_token_embeddings_workspace(0, 4096, 128) == 0
+
+
+def gl(L, x=P, n=1024, din=512, ldx=512, b=64, kept=P, nk=P, w=P, dout=256, ldw=512, y=P, ldy=256, cap=1024,
+       pad=256):
+    return L.lemo_gather_linear(x, n, din, ldx, b, kept, nk, w, dout, ldw, y, ldy, cap, pad, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID), (dict(x=NULL), INVALID), (dict(w=NULL), INVALID),
+    (dict(y=NULL), INVALID), (dict(n=1000), INVALID), (dict(cap=0), INVALID), (dict(pad=0), INVALID),
+    (dict(dout=0), INVALID), (dict(ldw=256), INVALID), (dict(ldy=128), INVALID),
+    (dict(din=96, ldx=96, ldw=96), UNSUP), (dict(x=P2), ALIGN), (dict(w=P2), ALIGN), (dict(ldy=260), ALIGN),
+])
+def test_gather_linear_rejects(L, kw, status):
+    assert gl(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def ls(L, a=P, din=512, lda=512, cap=1024, w=P, dout=256, ldw=512, res=P, n=1024, ldr=256, b=64, kept=P, nk=P):
+    return L.lemo_linear_scatter(a, din, lda, cap, w, dout, ldw, res, n, ldr, b, kept, nk, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID), (dict(a=NULL), INVALID), (dict(w=NULL), INVALID),
+    (dict(res=NULL), INVALID), (dict(n=1000), INVALID), (dict(cap=0), INVALID), (dict(b=0), INVALID),
+    (dict(lda=256), INVALID), (dict(ldr=128), INVALID),
+    (dict(din=96, lda=96, ldw=96), UNSUP), (dict(a=P2), ALIGN), (dict(res=P2), ALIGN), (dict(ldr=260), ALIGN),
+])
+def test_linear_scatter_rejects(L, kw, status):
+    assert ls(L, **kw) == status
+    assert lemo.lemo_last_error()
 
 
 def sel(L, s=P, nb=256, mode=1, th=0.0, k=10, mask=P, kept=P, nk=P):

@@ -606,3 +606,140 @@ def test_token_embeddings_deterministic():
     a = lemo.lemo_token_embeddings(dev(x), *[dev(t) for t in w])
     b = lemo.lemo_token_embeddings(dev(x), *[dev(t) for t in w])
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------- movement fused into the products
+FUSED = [
+    # (N, d_in, d_out, block, keep fraction, pad_multiple, cap extra rows)
+    (512, 128, 96, 16, 0.5, 64, 8),
+    (1024, 256, 256, 64, 0.4, 256, 0),
+    (640, 64, 200, 32, 1.0, 1, 0),        # keep all, ragged d_out
+    (512, 128, 128, 64, 0.0, 64, 3),      # keep none
+]
+
+
+def _fused_case(case, seed):
+    n, din, dout, b, frac, pad, extra = case
+    rng = np.random.default_rng(seed)
+    nb = n // b
+    kept = _kept_from_mask(rng, nb, frac)
+    x = synth.random_bf16(rng, (n, din))
+    w = synth.random_bf16(rng, (dout, din), 1.0 / math.sqrt(din))
+    R = kept.size * b
+    cap = max(1, -(-R // pad) * pad + extra)
+    return n, din, dout, b, pad, kept, x, w, R, cap, rng
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "N%d_in%d_out%d_b%d_keep%.1f" % c[:5])
+def test_gather_linear(case):
+    n, din, dout, b, pad, kept, x, w, R, cap, rng = _fused_case(case, 31)
+    say("gather_linear", case)
+    sentinel = np.full((cap, dout), 0x5A5A, np.uint16)
+    ref, over = O.gather_linear(x, b, kept, kept.size, w, sentinel, pad)
+    kd = dev(kept) if kept.size else torch.zeros(1, dtype=torch.int32, device="cuda")
+    nkd = dev(np.array([kept.size], np.int32))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    yd = dev(sentinel)
+    lemo.lemo_gather_linear(dev(x), b, kd, nkd, dev(w), yd, pad_multiple=pad, dev_status=status)
+    got = host_bits(yd)
+    if R:
+        ok, same = _embeddings_close(got[:R], ref[:R])
+        assert ok, same
+    assert np.array_equal(got[R:], ref[R:])          # zero padding and untouched rows, bit-exact
+    assert int(status.item()) == 0 and not over
+    # the gather in the operand prologue equals gathering first (same product)
+    if R:
+        xg = torch.zeros((cap, din), dtype=torch.int16, device="cuda")
+        lemo.lemo_gather_pad(dev(x), b, kd, nkd, xg)
+        ident = dev(np.arange(cap // b + 1, dtype=np.int32))
+        y2 = dev(sentinel)
+        lemo.lemo_gather_linear(xg, b, ident, nkd, dev(w), y2, pad_multiple=pad, n_tokens=(cap // b) * b)
+        assert torch.equal(y2[:R], yd[:R])
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "N%d_in%d_out%d_b%d_keep%.1f" % c[:5])
+def test_linear_scatter(case):
+    n, din, dout, b, pad, kept, x, w, R, cap, rng = _fused_case(case, 37)
+    say("linear_scatter", case)
+    a = synth.random_bf16(rng, (max(R, 1), din))
+    res = synth.random_bf16(rng, (n, dout))
+    ref = O.linear_scatter(a, w, res, b, kept, kept.size)
+    kd = dev(kept) if kept.size else torch.zeros(1, dtype=torch.int32, device="cuda")
+    nkd = dev(np.array([kept.size], np.int32))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rd = dev(res)
+    lemo.lemo_linear_scatter(dev(a), dev(w), rd, b, kd, nkd, dev_status=status)
+    got = host_bits(rd)
+    rows = O.kept_token_rows(kept, kept.size, b)
+    dropped = np.setdiff1d(np.arange(n), rows)
+    assert np.array_equal(got[dropped], res[dropped])     # untouched rows, bit-exact
+    if R:
+        ok, same = _embeddings_close(got[rows], ref[rows])
+        assert ok, same
+    assert int(status.item()) == 0
+    # the addition in the epilogue equals the product followed by the plain scatter
+    if R:
+        ident = dev(np.arange(R // b, dtype=np.int32))
+        y = torch.zeros((R, dout), dtype=torch.int16, device="cuda")
+        lemo.lemo_gather_linear(dev(a[:R]), b, ident, nkd, dev(w), y)
+        r2 = dev(res)
+        lemo.lemo_scatter_residual(r2, b, kd, nkd, y)
+        assert torch.equal(r2, rd)
+
+
+def test_fused_bad_kept_and_capacity():
+    n, din, dout, b = 256, 64, 64, 16
+    rng = np.random.default_rng(41)
+    x = synth.random_bf16(rng, (n, din))
+    w = synth.random_bf16(rng, (dout, din), 0.125)
+    kept = np.array([1, 40, 3], np.int32)                  # 40 is out of range
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = dev(np.full((48, dout), 0x5A5A, np.uint16))
+    lemo.lemo_gather_linear(dev(x), b, dev(kept), dev(np.array([3], np.int32)), dev(w), y, dev_status=status)
+    got = host_bits(y)
+    assert np.all(got[16:32] == 0x5A5A)                     # the invalid block's rows are skipped
+    ref = O.linear_bf16(x[16:32], w)
+    ok, _ = _embeddings_close(got[0:16], ref)
+    assert ok and int(status.item()) & lemo.DEV_BAD_KEPT
+    status.zero_()
+    y = dev(np.full((20, dout), 0x5A5A, np.uint16))          # 2 kept blocks = 32 rows > 20
+    lemo.lemo_gather_linear(dev(x), b, dev(np.array([2, 5], np.int32)), dev(np.array([2], np.int32)), dev(w), y,
+                            pad_multiple=1, dev_status=status)
+    assert int(status.item()) & lemo.DEV_CAP_OVERFLOW
+    ok, _ = _embeddings_close(host_bits(y), O.linear_bf16(np.concatenate([x[32:48], x[80:84]]), w))
+    assert ok
+
+
+def test_fused_full_size_sampled():
+    """Llama2-7B shape: the query projection (4096 x 4096) on the kept rows of
+    the oracle's mask with the gather fused in, and the output projection
+    added back into the residual stream; rows checked on a sample."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("fused full size")
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, rank=w.rank, planted_frac=w.planted_frac)
+    _, I_ref, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
+    _, kept, nk, _ = O.select_mask(I_ref.astype(np.float32), O.SELECT_MEAN)
+    R = nk * w.block
+    rng = np.random.default_rng(43)
+    wq = synth.random_bf16(rng, (w.d_model, w.d_model), 1.0 / math.sqrt(w.d_model))
+    kd, nkd = dev(kept), dev(np.array([nk], np.int32))
+    cap = -(-R // 256) * 256
+    y = torch.empty((cap, w.d_model), dtype=torch.int16, device="cuda")
+    lemo.lemo_gather_linear(dev(L.x), w.block, kd, nkd, dev(wq), y, pad_multiple=256)
+    rows = O.kept_token_rows(kept, nk, w.block)
+    sample = np.sort(rng.choice(R, size=64, replace=False))
+    got = host_bits(y)
+    ok, same = _embeddings_close(got[sample], O.linear_bf16(L.x[rows[sample]], wq))
+    assert ok, same
+    assert np.all(got[R:] == 0)
+    # the output projection of a stand-in attention output (seeded, R rows)
+    a = synth.random_bf16(rng, (R, w.d_model))
+    resd = dev(L.x)
+    lemo.lemo_linear_scatter(dev(a), dev(wq), resd, w.block, kd, nkd)
+    res = host_bits(resd)
+    dropped = np.setdiff1d(np.arange(w.n_tokens), rows)
+    assert np.array_equal(res[dropped], L.x[dropped])
+    ref = O.scatter_residual(L.x[rows[sample]], 1, np.arange(sample.size, dtype=np.int32), sample.size,
+                             O.linear_bf16(a[sample], wq))
+    ok, same = _embeddings_close(res[rows[sample]], ref)
+    assert ok, same
