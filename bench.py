@@ -230,6 +230,7 @@ def main():
         "clock_settle_steps": settle_steps,
     }
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
+    out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -272,6 +273,58 @@ def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):
     return {"embeddings_ms": t_e, "scores_ms": t_s,
             "embeddings_TFLOPs": f_e / (t_e * 1e-3) / 1e12, "scores_TFLOPs": f_s / (t_s * 1e-3) / 1e12,
             "tokens_per_s": N / ((t_e + t_s) * 1e-3)}
+
+
+def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
+    """Token movement fused into the layer's products on the same layer and
+    mask: the kept-row gather feeding a d x d projection (lemo_gather_linear)
+    and a d x d projection added back into the residual stream
+    (lemo_linear_scatter), each against the stand-alone movement call plus the
+    same product.  Mean event times over `reps` calls after 3 warm-up calls."""
+    import torch
+    from contextual_token_sparsity_amd import lemo
+    R = nk * b
+    cap = -(-R // 256) * 256
+    g = torch.Generator(device=dev).manual_seed(123)
+    w = (torch.randn(d, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    a = torch.randn(cap, d, device=dev, generator=g).to(torch.bfloat16)
+    y = torch.empty((cap, d), dtype=torch.int16, device=dev)
+    xg = torch.empty((cap, d), dtype=torch.int16, device=dev)
+    y2 = torch.empty((R, d), dtype=torch.int16, device=dev)
+    ident = torch.arange(cap // b, dtype=torch.int32, device=dev)
+
+    def gather_fused():
+        lemo.lemo_gather_linear(x, b, kept, n_kept, w, y, pad_multiple=256)
+
+    def gather_unfused():
+        lemo.lemo_gather_pad(x, b, kept, n_kept, xg, pad_multiple=256)
+        lemo.lemo_gather_linear(xg, b, ident, n_kept, w, y, pad_multiple=256, n_tokens=cap)
+
+    def scatter_fused():
+        lemo.lemo_linear_scatter(a[:R], w, resid, b, kept, n_kept)
+
+    def scatter_unfused():
+        lemo.lemo_gather_linear(a[:R], b, ident, n_kept, w, y2, n_tokens=R)
+        lemo.lemo_scatter_residual(resid, b, kept, n_kept, y2)
+
+    res = {}
+    for name, fn in (("gather_linear", gather_fused), ("gather_then_linear", gather_unfused),
+                     ("linear_scatter", scatter_fused), ("linear_then_scatter", scatter_unfused)):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_ms"] = e0.elapsed_time(e1) / reps
+    flops = 2.0 * R * d * d
+    res["kept_rows"] = R
+    res["gather_linear_TFLOPs"] = flops / (res["gather_linear_ms"] * 1e-3) / 1e12
+    res["linear_scatter_TFLOPs"] = flops / (res["linear_scatter_ms"] * 1e-3) / 1e12
+    return res
 
 
 def movement_cold(gx, ga, sc, stream, dev, reps=5):

@@ -215,6 +215,7 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
           n_tokens, block, d_in, d_out, cap_rows, pad_multiple);
   REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
+  REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_in, "x")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
@@ -235,6 +236,7 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
           cap_rows);
   REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
+  REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
   lemo_status st;
   if ((st = check_rows(a, ld_a, d_in, "a")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;

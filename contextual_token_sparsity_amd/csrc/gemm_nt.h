@@ -3,13 +3,20 @@
 // Device code shared by the per-token predictor and the fused movement
 // products; each translation unit gets its own copy (internal linkage).
 //
-// One 64 x 128 tile of C per workgroup of 4 waves (32 x 64 per wave as 1 x 2
-// v_mfma_f32_32x32x16_bf16 tiles).  The reduction streams in 64-wide chunks
-// through a 3-stage LDS ring filled by direct global->LDS loads (two chunks in
-// flight), with the 16-byte pieces of each 128-B LDS row XOR-swizzled so that
+// One TM x 128 tile of C per workgroup of 4 waves (TM/2 x 64 per wave as
+// TM/64 x 2 v_mfma_f32_32x32x16_bf16 tiles).  TM = 64 suits a narrow B (more
+// workgroups: the predictor's 16384 x 256 hidden layer still spreads over 512);
+// TM = 128 suits a square weight (each operand fragment feeds two MFMAs).  The
+// reduction streams in 64-wide chunks through an LDS ring filled by direct
+// global->LDS loads (3 stages for TM = 64, two chunks in flight; 2 stages for
+// TM = 128, so that two workgroups still fit on a CU), with the 16-byte
+// pieces of each 128-B LDS row XOR-swizzled so that
 // the operand reads are free of bank conflicts.  Workgroup ids go round-robin
-// over the 8 XCDs; the column tiles of one row block are given to ids on the
-// same XCD, back to back, so the second read of those rows of A hits L2.
+// over the 8 XCDs; when there are few column tiles (a narrow B, e.g. the
+// predictor's hidden layer), the column tiles of one row block are given to
+// ids on the same XCD, back to back, so the second read of those rows of A
+// hits L2; with many column tiles (a d x d weight) the plain row-major order
+// keeps each XCD on a quarter of B instead.
 //
 // Epilogues (EPI):
 //   kEpiReluBf16   C[m][n] = bf16(max(0, acc))                       (dense rows)
@@ -30,23 +37,25 @@ namespace {
 
 namespace gemm {
 
-constexpr int kTM = 64;                             // tile rows (A)
 constexpr int kTN = 128;                            // tile columns (B rows)
-constexpr int kWaves = 4;                           // 2 x 2 waves of 32 x 64
+constexpr int kWaves = 4;                           // 2 x 2 waves of TM/2 x 64
 constexpr int kThreads = kWaves * 64;
 constexpr int kChunk = 64;                          // reduction elements per stage
 constexpr int kRowBytes = kChunk * 2;               // 128 B
-constexpr int kRegionA = kTM * kRowBytes;           // 8 KiB
 constexpr int kRegionB = kTN * kRowBytes;           // 16 KiB
-constexpr int kStageBytes = kRegionA + kRegionB;
-constexpr int kDmaA = kRegionA / (kThreads * 16);   // 2 loads of 16 B per thread
-constexpr int kDmaB = kRegionB / (kThreads * 16);   // 4
-constexpr int kStages = 3;                          // 72 KiB: two workgroups per CU
-constexpr int kDmaPerChunk = kDmaA + kDmaB;
+constexpr int kDmaB = kRegionB / (kThreads * 16);   // 4 loads of 16 B per thread
+
+template <int TM>
+struct Tile {
+  static constexpr int kRegionA = TM * kRowBytes;             // 8 or 16 KiB
+  static constexpr int kStageBytes = kRegionA + kRegionB;
+  static constexpr int kDmaA = kRegionA / (kThreads * 16);    // 2 or 4
+  static constexpr int kStages = TM == 64 ? 3 : 2;            // 72 or 64 KiB: two workgroups per CU
+  static constexpr int kDmaPerChunk = kDmaA + kDmaB;
+  static constexpr int kMT = TM / 64;                         // MFMA row tiles per wave
+};
 
 enum { kEpiReluBf16 = 0, kEpiBf16 = 1, kEpiGather = 2, kEpiScatterAdd = 3 };
-
-__shared__ __attribute__((aligned(1024))) uint8_t g_tile[kStages * kStageBytes];
 
 // Piece swizzle of LDS row r (distinct for 8 consecutive rows and for the 8
 // even/odd rows among 16 consecutive rows).
@@ -77,11 +86,16 @@ struct RowMap {
 };
 
 // C[m][n] = sum_k A[m][k] B[n][k] for m < M (the row capacity of C for the
-// gather epilogue), n < Nn; K a multiple of 64.  Rows of A (B) past the rows
+// gather epilogue), n < Nn; K a multiple of 64, Nn and ldc multiples of 8.  Rows of A (B) past the rows
 // in use read a valid row, and their results are dropped.
-template <int EPI>
+template <int EPI, int TM>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ldb, int M, int Nn, int K, int ldc,
                                                          int tm_count, int tn_count, RowMap rm) {
+  using T = Tile<TM>;
+  constexpr int kRegionA = T::kRegionA, kStageBytes = T::kStageBytes, kDmaA = T::kDmaA, kStages = T::kStages;
+  constexpr int kDmaPerChunk = T::kDmaPerChunk, kMT = T::kMT;
+  constexpr int kWM = TM / 2;                        // rows per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t g_tile[kStages * kStageBytes];
   constexpr bool kMapped = EPI == kEpiGather || EPI == kEpiScatterAdd;
   const uint16_t* __restrict__ A = g.a[blockIdx.z];
   const uint16_t* __restrict__ B = g.b[blockIdx.z];
@@ -89,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   int tm, tn;
   {
     const int w = blockIdx.x;
-    if (tm_count % 8 == 0) {
+    if (tm_count % 8 == 0 && tn_count <= 4) {
       const int j = w / 8;
       tn = j % tn_count;
       tm = (j / tn_count) * 8 + w % 8;
@@ -98,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
       tn = w % tn_count;
     }
   }
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int m0 = tm * TM, n0 = tn * kTN;
 
   // rows in use: all M, or the kept rows (plus zero padding for the gather)
   int R = M, rows_used = M, nb = 0;
@@ -176,34 +190,46 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int piece = (2 * s + hi) ^ swz(l32);
-    offA[s] = (uint32_t)((wq * 32 + l32) * kRowBytes + piece * 16);
+    offA[s] = (uint32_t)((wq * kWM + l32) * kRowBytes + piece * 16);
     offB[s] = (uint32_t)(kRegionA + (wk * 64 + l32) * kRowBytes + piece * 16);
   }
 
-  lemo_f32x16 acc[2];
+  lemo_f32x16 acc[kMT][2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int a = 0; a < kMT; ++a)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-  lemo_bf16x8 fa[2], fb[2][2];
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  lemo_bf16x8 fa[2][kMT], fb[2][2];
   auto read_frags = [&](int buf, const uint8_t* st, int s) {
-    fa[buf] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s]);
+#pragma unroll
+    for (int a = 0; a < kMT; ++a)
+      fa[buf][a] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + a * 32 * kRowBytes);
 #pragma unroll
     for (int i = 0; i < 2; ++i) fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
   };
 
   const int nchunks = K / kChunk;
+  static_assert(kStages == 2 || kStages == 3, "ring depth");
   issue(0, 0);
-  if (nchunks > 1) issue(1, 1);
+  if (kStages == 3 && nchunks > 1) issue(1, 1);
   for (int c = 0; c < nchunks; ++c) {
-    // this wave's loads of chunk c have landed (only chunk c+1's may still be
-    // in flight); after the barrier every wave's have, and every wave is done
-    // with chunk c-1's stage, which is refilled with chunk c+2
-    if (c + 1 < nchunks)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kDmaPerChunk) : "memory");
-    else
+    if constexpr (kStages == 3) {
+      // this wave's loads of chunk c have landed (only chunk c+1's may still
+      // be in flight); after the barrier every wave's have, and every wave is
+      // done with chunk c-1's stage, which is refilled with chunk c+2
+      if (c + 1 < nchunks)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kDmaPerChunk) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 2 < nchunks) issue(c + 2, (c + 2) % kStages);
+    } else {
+      // chunk c has landed everywhere after the barrier, and every wave is
+      // done with the other stage, which is refilled with chunk c+1
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 2 < nchunks) issue(c + 2, (c + 2) % kStages);
+      if (c + 1 < nchunks) issue(c + 1, (c + 1) % kStages);
+    }
     const uint8_t* st = g_tile + (c % kStages) * kStageBytes;
     read_frags(0, st, 0);
 #pragma unroll
@@ -212,45 +238,74 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
       if (s + 1 < 4) read_frags(cur ^ 1, st, s + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur], fb[cur][b], acc[b], 0, 0, 0);
+      for (int a = 0; a < kMT; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // epilogue, bounds-checked
+  // epilogue: the bf16 tile is staged in LDS (the ring is free once every
+  // wave is past the last chunk), then written with 16-byte row accesses
+  constexpr int kLdt = kTN + 8;                      // LDS row stride (elements)
+  static_assert(TM * kLdt * 2 <= kStages * kStageBytes, "staging tile fits the ring");
+  asm volatile("s_barrier" ::: "memory");
+  uint16_t* stile = reinterpret_cast<uint16_t*>(g_tile);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int row = m0 + wq * 32 + acc_row(lane, e);
-    if (row >= rows_used) continue;
-    int t = row;
-    if (kMapped && row < R) t = tok_of(row);
-    if (kMapped && row < R && t < 0) {
-      if (rm.status) atomicOr(rm.status, LEMO_DEV_BAD_KEPT);
-      continue;
-    }
+  for (int a = 0; a < kMT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int col = n0 + wk * 64 + b * 32 + l32;
-      if (col >= Nn) continue;
-      float v = acc[b][e];
-      if (EPI == kEpiReluBf16) v = fmaxf(v, 0.f);
-      if (EPI == kEpiScatterAdd) {
-        uint16_t* p = C + (size_t)t * ldc + col;
-        const float y = lemo_bf16_to_f32(lemo_f32_to_bf16(v));
-        *p = (uint16_t)lemo_f32_to_bf16(lemo_bf16_to_f32(*p) + y);
-      } else if (EPI == kEpiGather && row >= R) {
-        C[(size_t)row * ldc + col] = 0;   // zero padding
-      } else {
-        C[(size_t)row * ldc + col] = (uint16_t)lemo_f32_to_bf16(v);
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = acc[a][b][e];
+        if (EPI == kEpiReluBf16) v = fmaxf(v, 0.f);
+        stile[(wq * kWM + a * 32 + acc_row(lane, e)) * kLdt + wk * 64 + b * 32 + l32] = (uint16_t)lemo_f32_to_bf16(v);
       }
+  __syncthreads();
+  constexpr int kPieces = kTN / 8;                   // 16-byte pieces per tile row
+  for (int idx = tid; idx < TM * kPieces; idx += kThreads) {
+    const int r = idx / kPieces, c8 = idx % kPieces;
+    const int row = m0 + r, col = n0 + c8 * 8;
+    if (row >= rows_used || col >= Nn) continue;
+    const uint4 y = *reinterpret_cast<const uint4*>(stile + r * kLdt + c8 * 8);
+    if (EPI == kEpiBf16 || EPI == kEpiReluBf16) {
+      *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = y;
+    } else if (EPI == kEpiGather) {
+      uint4 out = y;
+      if (row >= R) {
+        out = make_uint4(0, 0, 0, 0);               // zero padding
+      } else if (tok_of(row) < 0) {
+        if (rm.status) atomicOr(rm.status, LEMO_DEV_BAD_KEPT);
+        continue;                                   // invalid kept block: row left as it is
+      }
+      *reinterpret_cast<uint4*>(C + (size_t)row * ldc + col) = out;
+    } else {
+      const int t = tok_of(row);
+      if (t < 0) {
+        if (rm.status) atomicOr(rm.status, LEMO_DEV_BAD_KEPT);
+        continue;
+      }
+      uint16_t* p = C + (size_t)t * ldc + col;
+      const uint4 res = *reinterpret_cast<const uint4*>(p);
+      const uint32_t* rw = &res.x;
+      const uint32_t* yw = &y.x;
+      uint4 o;
+      uint32_t* ow = &o.x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = lemo_bf16_to_f32(rw[j] & 0xffffu) + lemo_bf16_to_f32(yw[j] & 0xffffu);
+        const float hi2 = lemo_bf16_to_f32(rw[j] >> 16) + lemo_bf16_to_f32(yw[j] >> 16);
+        ow[j] = lemo_f32_to_bf16(lo) | (lemo_f32_to_bf16(hi2) << 16);
+      }
+      *reinterpret_cast<uint4*>(p) = o;
     }
   }
 }
 
-// Grid of k_gemm_nt: row tiles x column tiles, products in z.
-inline dim3 grid_for(int rows, int cols, int products, int& tm_count, int& tn_count) {
-  tm_count = (rows + kTM - 1) / kTM;
+// Grid of k_gemm_nt<., TM>: row tiles x column tiles, products in z.
+inline dim3 grid_for(int tile_rows, int rows, int cols, int products, int& tm_count, int& tn_count) {
+  tm_count = (rows + tile_rows - 1) / tile_rows;
   tn_count = (cols + kTN - 1) / kTN;
   return dim3(tm_count * tn_count, 1, products);
 }

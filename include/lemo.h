@@ -223,7 +223,8 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
  *   the kept rows densely, [cap_rows][ld_a] (d_in used); kept rows past
  *   cap_rows are skipped and flag LEMO_DEV_CAP_OVERFLOW.
  * Invalid kept indices are skipped and flag LEMO_DEV_BAD_KEPT.
- * d_in a multiple of 64.  Errors: INVALID_ARG, UNSUPPORTED (d_in), ALIGNMENT.
+ * d_in a multiple of 64, d_out a multiple of 8.  Errors: INVALID_ARG,
+ * UNSUPPORTED (d_in), ALIGNMENT (pointers, ld, d_out).
  * ------------------------------------------------------------------------ */
 lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int ld_x, int block,
                                const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* weight,

@@ -105,6 +105,7 @@ def gl(L, x=P, n=1024, din=512, ldx=512, b=64, kept=P, nk=P, w=P, dout=256, ldw=
     (dict(y=NULL), INVALID), (dict(n=1000), INVALID), (dict(cap=0), INVALID), (dict(pad=0), INVALID),
     (dict(dout=0), INVALID), (dict(ldw=256), INVALID), (dict(ldy=128), INVALID),
     (dict(din=96, ldx=96, ldw=96), UNSUP), (dict(x=P2), ALIGN), (dict(w=P2), ALIGN), (dict(ldy=260), ALIGN),
+    (dict(dout=12), ALIGN),
 ])
 def test_gather_linear_rejects(L, kw, status):
     assert gl(L, **kw) == status
@@ -120,6 +121,7 @@ def ls(L, a=P, din=512, lda=512, cap=1024, w=P, dout=256, ldw=512, res=P, n=1024
     (dict(res=NULL), INVALID), (dict(n=1000), INVALID), (dict(cap=0), INVALID), (dict(b=0), INVALID),
     (dict(lda=256), INVALID), (dict(ldr=128), INVALID),
     (dict(din=96, lda=96, ldw=96), UNSUP), (dict(a=P2), ALIGN), (dict(res=P2), ALIGN), (dict(ldr=260), ALIGN),
+    (dict(dout=12), ALIGN),
 ])
 def test_linear_scatter_rejects(L, kw, status):
     assert ls(L, **kw) == status
