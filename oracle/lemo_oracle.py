@@ -26,6 +26,9 @@ function that takes it):
     positive scores, then block max) and the per-head block max, clamped, then
     summed over heads;
   * the column aggregate sums the block score over every query block;
+  * causal variant: only pairs j < i take part; a ragged last block holds the
+    N mod b remaining tokens; a block pair with no pair taking part scores 0;
+    a batch is its sequences scored one by one;
   * a block's representative embedding is the mean of its rows;
   * the predictor is two matrices, ReLU(x U) V; x-bar and the hidden ReLU
     output are rounded to bf16, everything after stays real-valued; the block
@@ -92,22 +95,23 @@ def bf16_round(x) -> np.ndarray:
 # --------------------------------------------------------------------------
 def exact_block_scores(q, k, n_heads: int, head_dim: int, block: int,
                        head_reduce: int = REDUCE_PAPER,
-                       query_blocks=None, key_blocks=None):
+                       query_blocks=None, key_blocks=None, causal: bool = False):
     """Score blocks B^S_nm of the attention scores and their column aggregate.
 
     [Jenga] 4.2.1, Eq. 1: the interaction of tokens i and j is S_ij = Q_i K_j;
-    a token's informativeness sums S_ij over i != j.
-    [Jenga] 4.2.1, Eq. 2 and Figure 6 caption: the score matrix is cut into
-    blocks B^S_nm (query block n, key block m); positive scores are summed
-    over the heads and divided by N_head, and the block's score is the
-    largest such value inside the block.  The token-block score is the block
-    score aggregated along the column (over n).
-    [LeMo] "What carries the argument": the scores are raw pre-softmax ones.
+    Eq. 2: the block score keeps only positive values, averages over the heads
+    (1/N_head) and takes the maximum over the block; Figure 6 caption: the
+    block matrix is aggregated along each column, I[m] = sum_n M[n][m];
+    [LeMo] reading notes: the scores are the raw pre-softmax ones.
 
     Readings: S^h_ij = Q^h_i . K^h_j / sqrt(head_dim) (the scale of the
     attention formula; it does not change any ranking); pairs i == j are
     left out of the block max as in Eq. 1; the column aggregate runs over all
-    query blocks (no causal mask).  ``head_reduce``:
+    query blocks (no causal mask).  With ``causal`` (a variant for decoder
+    models, whose attention never pairs a query with a later key), only pairs
+    j < i take part.  When N is not a multiple of the block size the last
+    block holds the N mod b remaining tokens.  A block pair with no pair
+    taking part scores 0.  ``head_reduce``:
       REDUCE_PAPER   M[n,m] = max_{i in n, j in m, i != j} (1/H) sum_h max(0, S^h_ij)
       REDUCE_HEADMAX M[n,m] = sum_h max(0, max_{i in n, j in m, i != j} S^h_ij)
     I[m] = sum_n M[n,m].
@@ -118,32 +122,31 @@ def exact_block_scores(q, k, n_heads: int, head_dim: int, block: int,
     """
     q = np.asarray(q)
     n_tok = q.shape[0]
-    if n_tok % block:
-        raise ValueError("N must be a multiple of the block size")
-    nb = n_tok // block
+    nb = -(-n_tok // block)
     Q = bf16_decode(q).reshape(n_tok, n_heads, head_dim)
     K = bf16_decode(k).reshape(n_tok, n_heads, head_dim)
     qb = list(range(nb)) if query_blocks is None else list(query_blocks)
     kb = list(range(nb)) if key_blocks is None else list(key_blocks)
-    key_rows = np.concatenate([np.arange(m * block, (m + 1) * block) for m in kb])
-    Kt = np.ascontiguousarray(K[key_rows].transpose(1, 2, 0))      # [H][hd][len(kb)*b]
+    rows_of = [np.arange(m * block, min((m + 1) * block, n_tok)) for m in kb]
+    j_abs = np.concatenate(rows_of)                               # key token index of each column
+    seg_start = np.cumsum([0] + [len(r) for r in rows_of])[:-1]   # first column of each key block
+    Kt = np.ascontiguousarray(K[j_abs].transpose(1, 2, 0))        # [H][hd][columns]
     scale = 1.0 / math.sqrt(head_dim)
     M = np.empty((len(qb), len(kb)), dtype=np.float64)
     for a, n in enumerate(qb):
-        Qn = np.ascontiguousarray(Q[n * block:(n + 1) * block].transpose(1, 0, 2))  # [H][b][hd]
-        S = np.matmul(Qn, Kt) * scale                             # S^h_ij, [H][b][len(kb)*b]
-        # i == j happens only where key block m is the query block n itself
-        same = np.zeros((block, len(kb) * block), dtype=bool)
-        for col, m in enumerate(kb):
-            if m == n:
-                same[:, col * block:(col + 1) * block] = np.eye(block, dtype=bool)
+        i_abs = np.arange(n * block, min((n + 1) * block, n_tok))
+        Qn = np.ascontiguousarray(Q[i_abs].transpose(1, 0, 2))    # [H][rows][hd]
+        S = np.matmul(Qn, Kt) * scale                             # S^h_ij
+        # pairs that take no part: i == j, and every j > i in the causal variant
+        out = (j_abs[None, :] >= i_abs[:, None]) if causal else (j_abs[None, :] == i_abs[:, None])
         if head_reduce == REDUCE_PAPER:
-            Sbar = np.maximum(S, 0.0).sum(axis=0) / n_heads      # [b][len(kb)*b]
-            Sbar[same] = -np.inf
-            M[a] = Sbar.reshape(block, len(kb), block).max(axis=(0, 2))
+            Sbar = np.maximum(S, 0.0).sum(axis=0) / n_heads      # [rows][columns]
+            Sbar[out] = -np.inf
+            best = np.maximum.reduceat(Sbar.max(axis=0), seg_start)
+            M[a] = np.maximum(best, 0.0)
         elif head_reduce == REDUCE_HEADMAX:
-            S[:, same] = -np.inf
-            per_head = S.reshape(n_heads, block, len(kb), block).max(axis=(1, 3))  # [H][len(kb)]
+            S[:, out] = -np.inf
+            per_head = np.maximum.reduceat(S.max(axis=1), seg_start, axis=1)   # [H][len(kb)]
             M[a] = np.maximum(per_head, 0.0).sum(axis=0)
         else:
             raise ValueError("unknown head reduction")
@@ -151,11 +154,21 @@ def exact_block_scores(q, k, n_heads: int, head_dim: int, block: int,
     return M, I
 
 
-def exact_column_score(q, k, n_heads, head_dim, block, head_reduce, key_block):
+def exact_block_scores_batched(q, k, n_heads: int, head_dim: int, block: int,
+                               head_reduce: int = REDUCE_PAPER, causal: bool = False):
+    """A batch of independent sequences, q and k bf16 bits [B][N][n_heads*head_dim]:
+    the scores of each sequence on its own (no pair crosses sequences).
+    Returns M float64 [B][nb][nb] and I float64 [B][nb]."""
+    res = [exact_block_scores(q[b], k[b], n_heads, head_dim, block, head_reduce, causal=causal)
+           for b in range(len(q))]
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
+
+
+def exact_column_score(q, k, n_heads, head_dim, block, head_reduce, key_block, causal: bool = False):
     """I[m] of one key block, for sampled checks at sizes where the whole
     block matrix is too slow on the host ([Jenga] 4.2.1, Eq. 2 / Fig. 6)."""
     M, _ = exact_block_scores(q, k, n_heads, head_dim, block, head_reduce,
-                              key_blocks=[key_block], query_blocks=None)
+                              key_blocks=[key_block], query_blocks=None, causal=causal)
     return float(M[:, 0].sum()), M[:, 0]
 
 

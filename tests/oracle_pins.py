@@ -135,13 +135,44 @@ def check_exact_hand(o) -> list:
     M, I = o.exact_block_scores(q, k, 2, 1, 2, o.REDUCE_HEADMAX)
     _fail(out, np.array_equal(M, np.array(e2["M_headmax"])) and np.array_equal(I, np.array(e2["I_headmax"])),
           f"E2 headmax: {M.tolist()} {I.tolist()}")
+    # causal variant on the same tokens
+    e7 = g["E7_causal"]
+    one = e7["one_head"]
+    q = f2bits(np.array(one["q"])[:, None])
+    k = f2bits(np.array(one["k"])[:, None])
+    for mode in (o.REDUCE_PAPER, o.REDUCE_HEADMAX):
+        M, I = o.exact_block_scores(q, k, 1, 1, 2, mode, causal=True)
+        _fail(out, np.array_equal(M, np.array(one["M"])) and np.array_equal(I, np.array(one["I"])),
+              f"E7 one head mode {mode}: {M.tolist()} {I.tolist()}")
+    mask, kept, nk, th = o.select_mask(np.array(one["I"], np.float32), o.SELECT_MEAN)
+    _fail(out, mask.tolist() == one["mean_mask"] and float(th) == one["mean_threshold"],
+          f"E7 mean select: {mask.tolist()} {th}")
+    two = e7["two_heads"]
+    q = _heads_to_bits(two["q_heads"])
+    k = _heads_to_bits(two["k_heads"])
+    for mode, mk, ik in ((o.REDUCE_PAPER, "M_paper", "I_paper"), (o.REDUCE_HEADMAX, "M_headmax", "I_headmax")):
+        M, I = o.exact_block_scores(q, k, 2, 1, 2, mode, causal=True)
+        _fail(out, np.array_equal(M, np.array(two[mk])) and np.array_equal(I, np.array(two[ik])),
+              f"E7 two heads mode {mode}: {M.tolist()} {I.tolist()}")
+    # a ragged last block
+    e8 = g["E8_tail_block"]
+    q = f2bits(np.array(e8["q"])[:, None])
+    k = f2bits(np.array(e8["k"])[:, None])
+    for causal, mk, ik in ((False, "M", "I"), (True, "M_causal", "I_causal")):
+        for mode in (o.REDUCE_PAPER, o.REDUCE_HEADMAX):
+            M, I = o.exact_block_scores(q, k, 1, 1, 2, mode, causal=causal)
+            _fail(out, np.array_equal(M, np.array(e8[mk])) and np.array_equal(I, np.array(e8[ik])),
+                  f"E8 causal={causal} mode {mode}: {M.tolist()} {I.tolist()}")
     return out
 
 
-def brute_exact(qf, kf, H, hd, b, mode):
-    """Pure-Python scalar enumeration of Eq. 1/2 (tiny inputs only)."""
+def brute_exact(qf, kf, H, hd, b, mode, causal=False):
+    """Pure-Python scalar enumeration of Eq. 1/2 (tiny inputs only).  Blocks
+    are consecutive runs of b tokens, the last one possibly shorter; a pair
+    (i, j) takes part unless i == j, or j > i in the causal variant; a block
+    pair with no pair taking part scores 0."""
     N = len(qf)
-    nb = N // b
+    nb = (N + b - 1) // b
     c = 1.0 / math.sqrt(hd)
 
     def S(h, i, j):
@@ -150,9 +181,12 @@ def brute_exact(qf, kf, H, hd, b, mode):
     M = [[0.0] * nb for _ in range(nb)]
     for n in range(nb):
         for m in range(nb):
-            pairs = [(i, j) for i in range(n * b, n * b + b) for j in range(m * b, m * b + b) if i != j]
+            pairs = [(i, j) for i in range(n * b, min(n * b + b, N)) for j in range(m * b, min(m * b + b, N))
+                     if (j < i if causal else i != j)]
+            if not pairs:
+                continue
             if mode == 0:
-                M[n][m] = max(sum(max(0.0, S(h, i, j)) for h in range(H)) / H for i, j in pairs)
+                M[n][m] = max(0.0, max(sum(max(0.0, S(h, i, j)) for h in range(H)) / H for i, j in pairs))
             else:
                 M[n][m] = sum(max(0.0, max(S(h, i, j) for i, j in pairs)) for h in range(H))
     I = [sum(M[n][m] for n in range(nb)) for m in range(nb)]
@@ -167,17 +201,19 @@ def check_exact_bruteforce(o, seeds=range(6)) -> list:
         hd = int(rng.choice([1, 2, 4]))
         b = int(rng.choice([2, 4]))
         nb = int(rng.integers(1, 4))
-        N = nb * b
-        qf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
-        kf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
-        q, k = torch_bf16_bits(qf32), torch_bf16_bits(kf32)
-        qf = o.bf16_decode(q).tolist()
-        kf = o.bf16_decode(k).tolist()
-        for mode in (0, 1):
-            Mb, Ib = brute_exact(qf, kf, H, hd, b, mode)
-            M, I = o.exact_block_scores(q, k, H, hd, b, mode)
-            _fail(out, np.allclose(M, Mb, rtol=1e-12, atol=1e-12) and np.allclose(I, Ib, rtol=1e-12, atol=1e-12),
-                  f"bruteforce seed {s} mode {mode} H{H} hd{hd} b{b} nb{nb}")
+        qf32 = rng.standard_normal((nb * b + b - 1, H * hd)).astype(np.float32)
+        kf32 = rng.standard_normal((nb * b + b - 1, H * hd)).astype(np.float32)
+        tail = int(rng.integers(1, b))
+        for N, causal in ((nb * b, False), (nb * b, True), (nb * b - b + tail, False), (nb * b - b + tail, True)):
+            q, k = torch_bf16_bits(qf32[:N]), torch_bf16_bits(kf32[:N])
+            qf = o.bf16_decode(q).tolist()
+            kf = o.bf16_decode(k).tolist()
+            for mode in (0, 1):
+                Mb, Ib = brute_exact(qf, kf, H, hd, b, mode, causal)
+                M, I = o.exact_block_scores(q, k, H, hd, b, mode, causal=causal)
+                _fail(out, M.shape == Mb.shape and np.allclose(M, Mb, rtol=1e-12, atol=1e-12)
+                      and np.allclose(I, Ib, rtol=1e-12, atol=1e-12),
+                      f"bruteforce seed {s} mode {mode} causal {causal} H{H} hd{hd} b{b} N{N}")
     return out
 
 
@@ -257,6 +293,36 @@ def check_exact_invariants(o) -> list:
     # sub-matrix evaluation agrees with the full matrix
     Ms, _ = o.exact_block_scores(q, k, H, hd, b, o.REDUCE_PAPER, query_blocks=[4, 1], key_blocks=[2, 4, 0])
     _fail(out, np.array_equal(Ms, Mp[np.ix_([4, 1], [2, 4, 0])]), "sub-matrix evaluation differs")
+    for mode, M0 in ((o.REDUCE_PAPER, Mp), (o.REDUCE_HEADMAX, Mh)):
+        Mc, _ = o.exact_block_scores(q, k, H, hd, b, mode, causal=True)
+        lower = np.tril(np.ones((nb, nb), dtype=bool), -1)
+        # causal: nothing above the block diagonal; below it every pair has
+        # j < i, so those blocks equal the full-attention ones
+        _fail(out, not Mc[np.triu_indices(nb, 1)].any(), f"causal scores above the block diagonal (mode {mode})")
+        _fail(out, np.array_equal(Mc[lower], M0[lower]), f"causal lower blocks differ from full attention (mode {mode})")
+        _fail(out, np.all(Mc.diagonal() <= M0.diagonal()) and np.any(Mc.diagonal() < M0.diagonal()),
+              f"causal diagonal blocks not a strict subset of pairs (mode {mode})")
+        # causal: later tokens change nothing for earlier queries, whatever the
+        # length of the prefix (a ragged last block included)
+        for n_pre in (5 * b, 4 * b + 3, b + 1):
+            Mpre, _ = o.exact_block_scores(q[:n_pre], k[:n_pre], H, hd, b, mode, causal=True)
+            full_q = n_pre // b
+            _fail(out, np.array_equal(Mpre[:full_q], Mc[:full_q, :Mpre.shape[1]]),
+                  f"causal prefix of {n_pre} tokens changes earlier scores (mode {mode})")
+        # full attention on a ragged sequence: pairs of whole blocks are those
+        # of the sequence cut back to whole blocks
+        Mr, Ir = o.exact_block_scores(q[:4 * b + 3], k[:4 * b + 3], H, hd, b, mode)
+        Mw, _ = o.exact_block_scores(q[:4 * b], k[:4 * b], H, hd, b, mode)
+        _fail(out, Mr.shape == (5, 5) and np.array_equal(Mr[:4, :4], Mw) and np.array_equal(Ir, Mr.sum(axis=0)),
+              f"ragged tail changes whole-block scores (mode {mode})")
+    # a batch is its sequences scored one by one
+    qb = np.stack([q, k, q[::-1].copy()])
+    kb = np.stack([k, q, k])
+    for causal in (False, True):
+        MB, IB = o.exact_block_scores_batched(qb, kb, H, hd, b, o.REDUCE_PAPER, causal=causal)
+        for i in range(3):
+            Mi, Ii = o.exact_block_scores(qb[i], kb[i], H, hd, b, o.REDUCE_PAPER, causal=causal)
+            _fail(out, np.array_equal(MB[i], Mi) and np.array_equal(IB[i], Ii), f"batch item {i} causal={causal}")
     return out
 
 

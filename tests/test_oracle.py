@@ -28,8 +28,18 @@ def mutant(old: str, new: str):
 
 
 MUTATIONS = [
-    ("no_diagonal_exclusion", "Sbar[same] = -np.inf", "pass", [P.check_exact_hand]),
-    ("headmax_keeps_diagonal", "S[:, same] = -np.inf", "pass", [P.check_exact_bruteforce]),
+    ("no_diagonal_exclusion", "Sbar[out] = -np.inf", "pass", [P.check_exact_hand]),
+    ("headmax_keeps_diagonal", "S[:, out] = -np.inf", "pass", [P.check_exact_bruteforce]),
+    ("causal_keeps_diagonal", "(j_abs[None, :] >= i_abs[:, None]) if causal", "(j_abs[None, :] > i_abs[:, None]) if causal",
+     [P.check_exact_hand]),
+    ("causal_reversed", "(j_abs[None, :] >= i_abs[:, None]) if causal", "(j_abs[None, :] <= i_abs[:, None]) if causal",
+     [P.check_exact_hand]),
+    ("tail_block_dropped", "nb = -(-n_tok // block)", "nb = n_tok // block", [P.check_exact_hand]),
+    ("tail_block_full_width", "rows_of = [np.arange(m * block, min((m + 1) * block, n_tok)) for m in kb]",
+     "rows_of = [np.arange(m * block, (m + 1) * block) % n_tok for m in kb]", [P.check_exact_bruteforce]),
+    ("empty_block_pair_not_zero", "M[a] = np.maximum(best, 0.0)", "M[a] = best", [P.check_exact_hand]),
+    ("batch_shares_first_sequence", "res = [exact_block_scores(q[b], k[b],", "res = [exact_block_scores(q[0], k[0],",
+     [P.check_exact_invariants]),
     ("transposed_column_sum", "I = M.sum(axis=0) if query_blocks", "I = M.sum(axis=1) if query_blocks",
      [P.check_exact_hand]),
     ("no_sqrt_scale", "scale = 1.0 / math.sqrt(head_dim)", "scale = 1.0", [P.check_exact_closed_form]),
