@@ -229,6 +229,7 @@ def main():
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
     }
+    out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
     if args.copy_probe:
@@ -244,6 +245,29 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, w)
     print(json.dumps(out), flush=True)
+
+
+def causal_scores(q, k, N, H, hd, b, mode, stream, dev, reps=10):
+    """The causal variant of the exact scores on the same Q and K
+    (lemo_block_scores_batched with the causal flag: only the tiles on or
+    below the diagonal are launched).  Algorithmic work: the N (N - 1) / 2
+    pairs j < i, 2 hd flops per pair and head.  Mean event times over `reps`
+    calls after 3 warm-up calls."""
+    import torch
+    from contextual_token_sparsity_amd import lemo
+    nb = N // b
+    I = torch.empty((1, nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(lemo.lemo_block_scores_batched_workspace(1, N, b), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + 3)]
+    for i in range(reps + 3):
+        ev[i][0].record(stream)
+        lemo.lemo_block_scores_batched(q, k, H, hd, b, mode, causal=True, scores=I, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[3:]]))
+    flops = 2.0 * hd * H * N * (N - 1) / 2
+    tf = flops / (t * 1e-3) / 1e12
+    return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3)}
 
 
 def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):

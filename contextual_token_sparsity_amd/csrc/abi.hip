@@ -62,6 +62,10 @@ const char* lemo_last_error(void) { return g_last_error.c_str(); }
 
 int lemo_version(void) { return 100; }  // 0.1.0
 
+// Exact scores: the tile grid (at most (N/128)^2 workgroups) stays within a
+// launch's 2^31 workgroups and the block matrix within 2^40 entries.
+constexpr int kMaxScoreTokens = 1 << 22;
+
 size_t lemo_block_scores_workspace(int n_tokens, int block) {
   if (n_tokens <= 0 || block <= 0 || n_tokens % block) return 0;
   const size_t nb = (size_t)(n_tokens / block);
@@ -76,6 +80,7 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
           "sizes must be positive (n_tokens=%d block=%d n_heads=%d head_dim=%d)", n_tokens, block, n_heads,
           head_dim);
   REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(n_tokens <= kMaxScoreTokens, LEMO_ERR_UNSUPPORTED, "n_tokens %d (at most %d)", n_tokens, kMaxScoreTokens);
   REQUIRE(head_reduce == LEMO_REDUCE_PAPER || head_reduce == LEMO_REDUCE_HEADMAX, LEMO_ERR_INVALID_ARG,
           "unknown head_reduce %d", head_reduce);
   REQUIRE((long long)n_heads * head_dim <= (1LL << 30), LEMO_ERR_INVALID_ARG, "n_heads*head_dim too large");
@@ -94,9 +99,67 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
             "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
     m_out = static_cast<float*>(workspace);
   }
-  return device_status(lemo_launch_block_scores(q, k, n_tokens, n_heads, head_dim, ld_q, ld_k, block, head_reduce,
-                                                m_out, scores, static_cast<hipStream_t>(stream)),
+  return device_status(lemo_launch_block_scores(q, k, 1, n_tokens, n_heads, head_dim, ld_q, ld_k, 0, 0, block,
+                                                head_reduce, false, m_out, scores, static_cast<hipStream_t>(stream)),
                        "lemo_block_scores launch");
+}
+
+size_t lemo_block_scores_batched_workspace(int n_batch, int n_tokens, int block) {
+  if (n_batch <= 0 || n_tokens <= 0 || block <= 0) return 0;
+  const size_t nb = (size_t)((n_tokens + block - 1) / block);
+  return lemo_align256((size_t)n_batch * nb * nb * sizeof(float));
+}
+
+lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, int n_batch, int n_tokens,
+                                      int n_heads, int head_dim, int ld_q, int ld_k, int64_t batch_stride_q,
+                                      int64_t batch_stride_k, int block, int head_reduce, int flags,
+                                      float* block_scores, float* scores, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  REQUIRE(scores != nullptr, LEMO_ERR_INVALID_ARG, "scores is NULL");
+  REQUIRE(n_batch > 0 && n_tokens > 0 && block > 0 && n_heads > 0 && head_dim > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_batch=%d n_tokens=%d block=%d n_heads=%d head_dim=%d)", n_batch, n_tokens,
+          block, n_heads, head_dim);
+  REQUIRE(n_batch <= 65535, LEMO_ERR_UNSUPPORTED, "n_batch %d (at most 65535)", n_batch);
+  REQUIRE(n_tokens <= kMaxScoreTokens, LEMO_ERR_UNSUPPORTED, "n_tokens %d (at most %d)", n_tokens, kMaxScoreTokens);
+  REQUIRE((flags & ~LEMO_SCORES_CAUSAL) == 0, LEMO_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  REQUIRE(head_reduce == LEMO_REDUCE_PAPER || head_reduce == LEMO_REDUCE_HEADMAX, LEMO_ERR_INVALID_ARG,
+          "unknown head_reduce %d", head_reduce);
+  REQUIRE((long long)n_heads * head_dim <= (1LL << 30), LEMO_ERR_INVALID_ARG, "n_heads*head_dim too large");
+  REQUIRE(head_dim == 64 || head_dim == 128, LEMO_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
+  REQUIRE(block == 32 || block == 64 || block == 128, LEMO_ERR_UNSUPPORTED, "block %d (32, 64 or 128 supported)",
+          block);
+  REQUIRE(head_reduce == LEMO_REDUCE_PAPER || n_heads <= 128, LEMO_ERR_UNSUPPORTED,
+          "HEADMAX supports at most 128 heads (got %d)", n_heads);
+  const int nb = (n_tokens + block - 1) / block;
+  const long long ntq = (n_tokens + 127) / 128;
+  const long long tiles = (flags & LEMO_SCORES_CAUSAL) ? ntq * (ntq + 1) / 2 : ntq * ntq;
+  REQUIRE(n_batch * tiles <= 0x7fffffffLL, LEMO_ERR_UNSUPPORTED,
+          "n_batch * tiles = %lld exceeds one launch (n_batch=%d n_tokens=%d)", n_batch * tiles, n_batch, n_tokens);
+  lemo_status st;
+  if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
+  if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
+  if (n_batch > 1) {
+    // each sequence's rows are 16-byte aligned, and sequences do not overlap
+    REQUIRE(batch_stride_q % 8 == 0 && batch_stride_k % 8 == 0, LEMO_ERR_ALIGNMENT,
+            "batch strides must be multiples of 8 elements (got %lld, %lld)", (long long)batch_stride_q,
+            (long long)batch_stride_k);
+    REQUIRE(batch_stride_q >= (int64_t)n_tokens * ld_q && batch_stride_k >= (int64_t)n_tokens * ld_k,
+            LEMO_ERR_INVALID_ARG, "batch strides (%lld, %lld) smaller than a sequence (%lld, %lld)",
+            (long long)batch_stride_q, (long long)batch_stride_k, (long long)n_tokens * ld_q,
+            (long long)n_tokens * ld_k);
+  }
+  float* m_out = block_scores;
+  if (!m_out) {
+    const size_t need = lemo_block_scores_batched_workspace(n_batch, n_tokens, block);
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    m_out = static_cast<float*>(workspace);
+  }
+  return device_status(lemo_launch_block_scores(q, k, n_batch, n_tokens, n_heads, head_dim, ld_q, ld_k,
+                                                n_batch > 1 ? batch_stride_q : 0, n_batch > 1 ? batch_stride_k : 0,
+                                                block, head_reduce, (flags & LEMO_SCORES_CAUSAL) != 0, m_out, scores,
+                                                static_cast<hipStream_t>(stream)),
+                       "lemo_block_scores_batched launch");
 }
 
 size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int rank) {

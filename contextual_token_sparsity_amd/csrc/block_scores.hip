@@ -30,13 +30,21 @@
 //           v_max_i32 starting from 0, which yields max(0, block max) (the
 //           clamp is free for the same reason), then across lanes; the clamped
 //           per-head maxima are summed over heads in head order.
-// The i == j pairs sit on the diagonal of diagonal sub-tiles; they are set to
-// 0, which changes neither reduction (PAPER values are >= 0, HEADMAX clamps at
-// 0).  The scale 1/sqrt(head_dim) (and 1/H for PAPER) is applied once to the
-// block value; every step is positively homogeneous so this is exact up to
+// Pairs that take no part are set to 0, which changes neither reduction
+// (PAPER values are >= 0, HEADMAX clamps at 0), and a block pair with none
+// left scores 0: the i == j pairs on the diagonal of diagonal sub-tiles; in
+// the causal variant (decoder attention pairs no query with a later key)
+// every j >= i; and, when N is not a multiple of the block size, the rows
+// past the sequence end that fill the last tile (loaded as copies of row
+// N-1).  Only waves whose 64 x 64 square holds such a pair test them.  The
+// scale 1/sqrt(head_dim) (and 1/H for PAPER) is applied once to the block
+// value; every step is positively homogeneous so this is exact up to
 // rounding.
 //
-// The column aggregate is a second, deterministic pass (k_colsum).
+// Causal launches cover only the tiles on or below the tile diagonal; each
+// tile below it also writes the zeros of its mirror tile above.  A batch of
+// independent sequences is the grid's y dimension.  The column aggregate is a
+// second, deterministic pass (k_colsum).
 #include <type_traits>
 
 #include "lemo_internal.h"
@@ -85,16 +93,21 @@ __device__ __forceinline__ int wave_imax(int v) {
   return v;
 }
 
-// Maps a linear workgroup id to a (query tile, key tile) pair.  Dispatch goes
+// Workgroup wg runs on XCD wg % 8 as its (wg / 8)-th workgroup there.  Give
+// XCD x the x-th of 8 contiguous ranges of the logical order (the first
+// total % 8 ranges one longer), so each XCD's L2 serves neighbouring tiles.
+__device__ __forceinline__ int xcd_logical(int wg, int total) {
+  const int x = wg % 8, base = total / 8, rem = total % 8;
+  return x * base + min(x, rem) + wg / 8;
+}
+
+// Maps a logical tile index to a (query tile, key tile) pair.  Dispatch goes
 // round-robin over the 8 XCDs; each XCD gets a contiguous range of logical
-// tiles, walked in groups of 8 query tiles so that the 64 workgroups
+// tiles (xcd_logical), walked in groups of 8 query tiles so that the 64 workgroups
 // resident on one XCD (2 per CU) cover an 8 x 8 patch of tiles and share Q
 // and K rows in that XCD's L2.  (Groups of 2, 4 or 16 rows, or a serpentine
 // walk, time within 1-2 % of this at N = 16384.)
-__device__ __forceinline__ void tile_of(int wg, int ntq, int ntk, int& tq, int& tk) {
-  const int total = ntq * ntk;
-  int logical = wg;
-  if (total % 8 == 0) logical = (wg % 8) * (total / 8) + wg / 8;
+__device__ __forceinline__ void tile_of(int logical, int ntq, int ntk, int& tq, int& tk) {
   constexpr int kGroup = 8;
   const int span = kGroup * ntk;
   const int g = logical / span;
@@ -105,23 +118,68 @@ __device__ __forceinline__ void tile_of(int wg, int ntq, int ntk, int& tq, int& 
   tk = in_group / rows;
 }
 
-template <int HD, int MODE, int BLK>
+// Causal launches: the tiles (tq, tk) with tk <= tq, ntq * (ntq + 1) / 2 of
+// them, in groups of 8 query tiles as in tile_of.  The
+// groups before group g hold the T(8g) tiles of query tiles < 8g, where
+// T(x) = x (x + 1) / 2; inside a group the key tiles left of the group's
+// first query tile are full columns of `rows` tiles, then the group's own
+// triangle follows row by row.
+__device__ __forceinline__ int tri(int x) { return x * (x + 1) / 2; }
+
+// the r with T(r) <= t < T(r + 1)
+__device__ __forceinline__ int tri_row(int t) {
+  int r = (int)((__builtin_sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while (tri(r + 1) <= t) ++r;
+  while (r > 0 && tri(r) > t) --r;
+  return r;
+}
+
+__device__ __forceinline__ void tri_tile_of(int logical, int ntq, int& tq, int& tk) {
+  constexpr int kGroup = 8;
+  const int first = (tri_row(logical) / kGroup) * kGroup;
+  const int rows = min(kGroup, ntq - first);
+  const int in_group = logical - tri(first);
+  if (in_group < rows * first) {
+    tq = first + in_group % rows;
+    tk = in_group / rows;
+  } else {
+    const int t = in_group - rows * first;
+    const int i = tri_row(t);
+    tq = first + i;
+    tk = first + t - tri(i);
+  }
+}
+
+template <int HD, int MODE, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int n_heads, int ldq,
-    int ldk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
+    int ldk, long long bsq, long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
   constexpr int kCPH = HD / kChunk;                      // chunks per head
   constexpr int kParts = (MODE == 1 && BLK == 128) ? kMaxHeadsHeadmax : 1;
   __shared__ float part[kWaves][kParts];                 // HEADMAX, 128-row blocks: per-head wave maxima
   __shared__ float fin[kWaves * 4];                      // final per-(wave, sub-tile) values
 
+  // the grid is (tiles per sequence) x (sequences); the batch's tiles form
+  // one logical order, sequence by sequence, split into XCD ranges
+  const int T = gridDim.x;
+  const int logical = xcd_logical(blockIdx.y * T + blockIdx.x, T * gridDim.y);
+  const int seq = logical / T;
   int tq, tk;
-  tile_of(blockIdx.x, ntq, ntk, tq, tk);
+  if (CAUSAL)
+    tri_tile_of(logical - seq * T, ntq, tq, tk);
+  else
+    tile_of(logical - seq * T, ntq, ntk, tq, tk);
+  Q += (size_t)seq * bsq;
+  K += (size_t)seq * bsk;
+  M += (size_t)seq * nb * nb;
   const int q0 = tq * kTQ, k0 = tk * kTK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = wave >> 1, wk = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
-  const bool diag_wave = (q0 + wq * 64) == (k0 + wk * 64);
+  // does this wave's 64 x 64 square hold a pair that takes no part?
+  const int qlo = q0 + wq * 64, klo = k0 + wk * 64;
+  const bool mask_wave = (CAUSAL ? klo >= qlo : klo == qlo) || qlo + 64 > n_tokens || klo + 64 > n_tokens;
   const uint32_t lds0 = (uint32_t)(uintptr_t)g_stage;
 
   // ---- per-lane DMA byte offsets: instruction i of this wave fills LDS
@@ -162,6 +220,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     offB[s] = (uint32_t)(kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
   }
 
+  // Zeroes the entries of sub-tile (a, b) whose pair takes no part: i == j
+  // (j >= i when causal), or a query or key row past the sequence end.
+  // Element e of this lane pairs query row qb + r_e (r_e = acc_row(lane, e)
+  // - 4 hi, a constant per e) with key row kr.  The empty asm makes both
+  // bases opaque, so the compares are redone at each call rather than hoisted
+  // out of the head loop as 64 live lane masks.
+  auto mask_tile = [&](lemo_f32x16& v, int a, int b) {
+    int qb = qlo + a * 32 + 4 * hi;
+    int kr = klo + b * 32 + l32;
+    asm volatile("" : "+v"(qb), "+v"(kr));
+    const int dq = kr - qb;                                  // i == j at r_e == dq
+    const int lim = kr >= n_tokens ? 0 : n_tokens - qb;      // rows r_e >= lim are out
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = 8 * (e >> 2) + (e & 3);
+      const bool out = (CAUSAL ? r <= dq : r == dq) || r >= lim;
+      if (out) v[e] = 0.f;
+    }
+  };
+
   lemo_f32x16 sum[2][2];          // PAPER: running sum over heads of max(0, S^h)
   lemo_f32x16 acc[2][2][2];       // [head parity][sub-tile]: S^h of the current and previous head
 #pragma unroll
@@ -185,11 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
       for (int e = 0; e < 16; ++e)
         sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
     } else {
-      if (diag_wave && a == b) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (acc_row(lane, e) == l32) acc[P][a][b][e] = 0.f;
-      }
+      if (mask_wave) mask_tile(acc[P][a][b], a, b);
       int m = BLK >= 64 ? hm_lane : 0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[P][a][b][e]));
@@ -295,12 +369,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 
   // ---- per-(wave, sub-tile) block values -> fin[]
   if (MODE == 0) {
-    if (diag_wave) {
+    if (mask_wave) {
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (acc_row(lane, e) == l32) sum[a][a][e] = 0.f;
+        for (int b = 0; b < 2; ++b) mask_tile(sum[a][b], a, b);
     }
     if (BLK >= 64) {
       int m = 0;
@@ -363,6 +436,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
         }
       }
       M[(size_t)bq * nb + bk] = val * out_scale;
+      // causal: the mirror tile (tk, tq) above the diagonal is not launched;
+      // its blocks have no pair with j < i
+      if (CAUSAL && tq != tk) M[(size_t)bk * nb + bq] = 0.f;
     }
   }
 }
@@ -374,6 +450,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 // deterministic.
 __global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ M, int nb, float* __restrict__ out) {
   __shared__ float partial[16][17];
+  M += (size_t)blockIdx.y * nb * nb;   // sequence blockIdx.y of a batch
+  out += (size_t)blockIdx.y * nb;
   const int col = blockIdx.x * 16 + (threadIdx.x & 15);
   const int slice = threadIdx.x >> 4;
   float s = 0.f;
@@ -391,45 +469,60 @@ __global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ M, int
   }
 }
 
-template <int HD, int MODE>
-hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n, int h, int ldq, int ldk, int block,
-                          float scale, float* m, int nb, hipStream_t st) {
+template <int HD, int MODE, bool CAUSAL>
+hipError_t launch_variant(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
+                          long long bsq, long long bsk, int block, float scale, float* m, int nb, hipStream_t st) {
   const int ntq = (n + kTQ - 1) / kTQ, ntk = (n + kTK - 1) / kTK;
-  const dim3 grid(ntq * ntk), blk(kThreads);
+  const dim3 grid(CAUSAL ? ntq * (ntq + 1) / 2 : ntq * ntk, n_batch), blk(kThreads);
   switch (block) {
     case 32:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 32>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 32, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
     case 64:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 64>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 64, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
     default:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 128>), grid, blk, 0, st, q, k, n, h, ldq, ldk, scale, m, nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 128, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
   }
   return hipGetLastError();
 }
 
+template <int HD, int MODE>
+hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
+                          long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
+                          hipStream_t st) {
+  return causal ? launch_variant<HD, MODE, true>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st)
+                : launch_variant<HD, MODE, false>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+}
+
 }  // namespace
 
-hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_colsum, dim3((nb + 15) / 16), dim3(256), 0, stream, m, nb, out);
+hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream, int n_batch) {
+  hipLaunchKernelGGL(k_colsum, dim3((nb + 15) / 16, n_batch), dim3(256), 0, stream, m, nb, out);
   return hipGetLastError();
 }
 
-hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_tokens, int n_heads,
-                                    int head_dim, int ld_q, int ld_k, int block, int head_reduce,
-                                    float* m_out, float* scores, hipStream_t stream) {
-  const int nb = n_tokens / block;
+hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_batch, int n_tokens, int n_heads,
+                                    int head_dim, int ld_q, int ld_k, long long bs_q, long long bs_k, int block,
+                                    int head_reduce, bool causal, float* m_out, float* scores, hipStream_t stream) {
+  const int nb = (n_tokens + block - 1) / block;
   const double c = 1.0 / __builtin_sqrt((double)head_dim);
   const float scale = (float)(head_reduce == 0 ? c / n_heads : c);
   hipError_t e;
   if (head_dim == 64)
-    e = head_reduce == 0 ? launch_hd_mode<64, 0>(q, k, n_tokens, n_heads, ld_q, ld_k, block, scale, m_out, nb, stream)
-                         : launch_hd_mode<64, 1>(q, k, n_tokens, n_heads, ld_q, ld_k, block, scale, m_out, nb, stream);
+    e = head_reduce == 0 ? launch_hd_mode<64, 0>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
+                                                 causal, scale, m_out, nb, stream)
+                         : launch_hd_mode<64, 1>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
+                                                 causal, scale, m_out, nb, stream);
   else
-    e = head_reduce == 0 ? launch_hd_mode<128, 0>(q, k, n_tokens, n_heads, ld_q, ld_k, block, scale, m_out, nb, stream)
-                         : launch_hd_mode<128, 1>(q, k, n_tokens, n_heads, ld_q, ld_k, block, scale, m_out, nb, stream);
+    e = head_reduce == 0 ? launch_hd_mode<128, 0>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
+                                                  causal, scale, m_out, nb, stream)
+                         : launch_hd_mode<128, 1>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
+                                                  causal, scale, m_out, nb, stream);
   if (e != hipSuccess) return e;
-  return lemo_launch_colsum(m_out, nb, scores, stream);
+  return lemo_launch_colsum(m_out, nb, scores, stream, n_batch);
 }

@@ -37,9 +37,12 @@ __device__ __forceinline__ float lemo_wave_max(float v) {
 }
 
 // Launchers (validated arguments only; return the hipError_t of the launch).
-hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_tokens, int n_heads,
-                                    int head_dim, int ld_q, int ld_k, int block, int head_reduce,
-                                    float* m_out, float* scores, hipStream_t stream);
+// n_batch sequences, sequence b at q + b*bs_q and k + b*bs_k (elements); M
+// and the scores of sequence b at m_out + b*nb*nb and scores + b*nb, where
+// nb = ceil(n_tokens / block).
+hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_batch, int n_tokens, int n_heads,
+                                    int head_dim, int ld_q, int ld_k, long long bs_q, long long bs_k, int block,
+                                    int head_reduce, bool causal, float* m_out, float* scores, hipStream_t stream);
 
 int lemo_predict_splitk(int nb, int d_model, int rank);
 size_t lemo_predict_ws_bytes(int n_tokens, int d_model, int block, int rank);
@@ -75,6 +78,6 @@ hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_re
                                const int32_t* kept, const int32_t* n_kept, const uint16_t* y, int ld_y,
                                int32_t* dev_status, hipStream_t stream);
 
-hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream);
+hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream, int n_batch = 1);
 
 static inline size_t lemo_align256(size_t x) { return (x + 255) & ~size_t(255); }

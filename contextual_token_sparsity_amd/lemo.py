@@ -21,11 +21,15 @@ LEMO_OK = 0
 REDUCE_PAPER, REDUCE_HEADMAX = 0, 1
 SELECT_THRESHOLD, SELECT_TOPK, SELECT_MEAN = 0, 1, 2
 DEV_CAP_OVERFLOW, DEV_NONFINITE, DEV_BAD_KEPT = 1, 2, 4
+LEMO_SCORES_CAUSAL = 1
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "lemo_block_scores_workspace": (_sz, [_i, _i]),
     "lemo_block_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lemo_block_scores_batched_workspace": (_sz, [_i, _i, _i]),
+    "lemo_block_scores_batched": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.c_int64, ctypes.c_int64, _i, _i, _i,
+                                       _vp, _vp, _vp, _sz, _vp]),
     "lemo_predict_scores_workspace": (_sz, [_i, _i, _i, _i]),
     "lemo_predict_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "lemo_token_embeddings_workspace": (_sz, [_i, _i, _i]),
@@ -120,6 +124,38 @@ def lemo_block_scores(q, k, n_heads: int, head_dim: int, block: int, head_reduce
                                  _ptr(block_scores), _ptr(scores), _ptr(workspace),
                                  workspace.numel() if workspace is not None else 0, _stream(q.device))
     _check(st, "lemo_block_scores")
+    return scores, block_scores
+
+
+def lemo_block_scores_batched_workspace(n_batch: int, n_tokens: int, block: int) -> int:
+    return lib().lemo_block_scores_batched_workspace(n_batch, n_tokens, block)
+
+
+def lemo_block_scores_batched(q, k, n_heads: int, head_dim: int, block: int, head_reduce: int = REDUCE_PAPER,
+                              causal: bool = False, block_scores=None, scores=None, workspace=None):
+    """Exact block scores of a batch.  q, k: [B][N][width] with unit column
+    stride (row stride and batch stride taken from the tensors) or [N][width]
+    for one sequence.  N need not be a multiple of block.  Returns (scores
+    [B][nb] fp32, block_scores [B][nb][nb] or None)."""
+    _bf16(q), _bf16(k)
+    if q.dim() == 2:
+        q, k = q.unsqueeze(0), k.unsqueeze(0)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[:2] != k.shape[:2] or q.stride(2) != 1 or k.stride(2) != 1:
+        raise ValueError("q and k must be [B][N][width] with unit column stride and the same B, N")
+    B, n = q.shape[0], q.shape[1]
+    nb = (n + block - 1) // block
+    if scores is None:
+        scores = torch.empty(B, nb, dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if block_scores is None:
+        ws_bytes = lemo_block_scores_batched_workspace(B, n, block)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().lemo_block_scores_batched(_ptr(q), _ptr(k), B, n, n_heads, head_dim, q.stride(1), k.stride(1),
+                                         q.stride(0), k.stride(0), block, head_reduce, LEMO_SCORES_CAUSAL if causal else 0,
+                                         _ptr(block_scores), _ptr(scores), _ptr(workspace),
+                                         workspace.numel() if workspace is not None else 0, _stream(q.device))
+    _check(st, "lemo_block_scores_batched")
     return scores, block_scores
 
 

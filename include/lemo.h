@@ -4,6 +4,7 @@
  * Per layer, the method decides which token blocks take part in the layer and
  * moves only those rows:
  *   exact block scores   lemo_block_scores      (pages: Eq. 1, Eq. 2, Figure 6)
+ *     batches, causal masking, ragged last block: lemo_block_scores_batched
  *   predicted scores     lemo_predict_scores    (pages: Eq. 3, Figure 8)
  *   per-token predictor  lemo_token_embeddings  (pages: Figure 8; scored by lemo_block_scores)
  *   threshold / compact  lemo_select_mask       (pages: layer threshold, Alg. 1 step 1)
@@ -95,7 +96,7 @@ typedef enum {
  *
  *  q, k          bf16 [n_tokens][ld_q|ld_k]; head h occupies columns
  *                h*head_dim .. h*head_dim+head_dim-1.
- *  n_tokens      N > 0, a multiple of block.
+ *  n_tokens      N > 0, a multiple of block, at most 2^22.
  *  head_dim      64 or 128.   block: 32, 64 or 128.
  *  block_scores  optional fp32 [nb][nb] output M (row n = query block),
  *                nb = n_tokens / block; NULL keeps M in the workspace.
@@ -103,14 +104,54 @@ typedef enum {
  *  workspace     device scratch of lemo_block_scores_workspace() bytes when
  *                block_scores is NULL; may be NULL / 0 bytes otherwise.
  * Errors: INVALID_ARG (null q/k/scores, N % block, n_heads < 1,
- * ld < n_heads*head_dim, bad head_reduce), UNSUPPORTED (head_dim, block),
- * ALIGNMENT, WORKSPACE.  Non-finite inputs give unspecified scores.
+ * ld < n_heads*head_dim, bad head_reduce), UNSUPPORTED (head_dim, block,
+ * N > 2^22), ALIGNMENT, WORKSPACE.  Non-finite inputs give unspecified scores.
  * ------------------------------------------------------------------------ */
 size_t lemo_block_scores_workspace(int n_tokens, int block); /* bytes needed when block_scores is NULL */
 lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_tokens, int n_heads,
                               int head_dim, int ld_q, int ld_k, int block, int head_reduce,
                               float* block_scores, float* scores, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Exact block scores of a batch of sequences, with a causal variant and a
+ * ragged last block (the same Eq. 1 / Eq. 2 / Figure 6 definitions).
+ *
+ * Sequence b (0 <= b < n_batch) has q + b*batch_stride_q and
+ * k + b*batch_stride_k as its [n_tokens][ld] matrices and is scored on its
+ * own: no pair crosses sequences.  n_tokens need not be a multiple of block:
+ * the last of nb = ceil(n_tokens / block) blocks holds the remaining tokens.
+ * With LEMO_SCORES_CAUSAL in flags only pairs j < i take part (decoder
+ * attention never pairs a query with a later key): every block above the
+ * block diagonal scores 0, diagonal blocks use their strictly lower pairs,
+ * and causal launches skip the tiles above the diagonal (about half the
+ * work).  Without the flag pairs i == j are excluded as in
+ * lemo_block_scores, which this call equals for n_batch = 1 and
+ * n_tokens % block == 0.  A block pair with no pair taking part scores 0.
+ *
+ *  n_batch        1..65535.
+ *  batch_stride_* elements between sequences: multiples of 8 and at least
+ *                 n_tokens*ld (sequences do not overlap); ignored when
+ *                 n_batch == 1.
+ *  flags          0 or LEMO_SCORES_CAUSAL.
+ *  block_scores   optional fp32 [n_batch][nb][nb] (sequence-major); NULL
+ *                 keeps M in the workspace.
+ *  scores         fp32 [n_batch][nb].
+ *  workspace      lemo_block_scores_batched_workspace() bytes when
+ *                 block_scores is NULL.
+ * Errors: as lemo_block_scores, plus INVALID_ARG (n_batch < 1, unknown
+ * flags, stride smaller than a sequence), UNSUPPORTED (n_batch > 65535, or
+ * n_batch times the 128 x 128 tiles of one sequence -- ceil(N/128)^2, or
+ * T(ceil(N/128)) = t (t + 1) / 2 with the causal flag -- above 2^31 - 1),
+ * ALIGNMENT (stride not a multiple of 8).
+ * ------------------------------------------------------------------------ */
+#define LEMO_SCORES_CAUSAL 1
+size_t lemo_block_scores_batched_workspace(int n_batch, int n_tokens, int block);
+lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, int n_batch, int n_tokens,
+                                      int n_heads, int head_dim, int ld_q, int ld_k, int64_t batch_stride_q,
+                                      int64_t batch_stride_k, int block, int head_reduce, int flags,
+                                      float* block_scores, float* scores, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Predicted block scores (Jenga 4.2.2, Eq. 3 and Figure 8).

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
 
@@ -56,6 +56,44 @@ def bs(L, q=P, k=P, n=1024, h=4, hd=128, ldq=512, ldk=512, b=64, mode=0, M=NULL,
 def test_block_scores_rejects(L, kw, status):
     assert bs(L, **kw) == status
     assert lemo.lemo_last_error()
+
+
+def test_block_scores_caps_tokens(L):
+    assert bs(L, n=(1 << 22) + 64) == UNSUP
+
+
+def bsb(L, q=P, k=P, B=2, n=1000, h=4, hd=128, ldq=512, ldk=512, sq=1000 * 512, sk=1000 * 512, b=64, mode=0,
+        flags=1, M=P, I=P, ws=NULL, wsb=0):
+    return L.lemo_block_scores_batched(q, k, B, n, h, hd, ldq, ldk, sq, sk, b, mode, flags, M, I, ws, wsb, NULL)
+
+
+def test_batched_workspace_query(L):
+    # ragged: 1000 tokens in blocks of 64 -> 16 blocks
+    assert L.lemo_block_scores_batched_workspace(3, 1000, 64) == 3 * 16 * 16 * 4
+    assert L.lemo_block_scores_batched_workspace(1, 16384, 64) == L.lemo_block_scores_workspace(16384, 64)
+    assert L.lemo_block_scores_batched_workspace(0, 1000, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=NULL), INVALID), (dict(q=NULL), INVALID), (dict(B=0), INVALID), (dict(n=0), INVALID),
+    (dict(flags=2), INVALID), (dict(flags=-1), INVALID), (dict(mode=3), INVALID), (dict(ldq=256), INVALID),
+    (dict(sq=999 * 512), INVALID), (dict(sk=-512), INVALID),
+    (dict(B=65536), UNSUP), (dict(hd=96, ldq=384, ldk=384, sq=384000, sk=384000), UNSUP), (dict(b=256), UNSUP),
+    (dict(n=(1 << 22) + 1, sq=1 << 32, sk=1 << 32), UNSUP),
+    (dict(B=3, n=1 << 22, sq=1 << 32, sk=1 << 32, flags=0), UNSUP),   # 3 x 2^30 tiles in one launch
+    (dict(q=P2), ALIGN), (dict(sq=1000 * 512 + 4), ALIGN),
+    (dict(M=NULL), WS), (dict(M=NULL, ws=P, wsb=100), WS),
+])
+def test_block_scores_batched_rejects(L, kw, status):
+    assert bsb(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def test_block_scores_batched_one_sequence_ignores_strides(L):
+    # n_batch == 1: strides that would be rejected for a batch are not looked
+    # at, so validation runs on to the (missing) workspace
+    assert bsb(L, B=1, sq=3, sk=-5, M=NULL) == WS
+    assert bsb(L, B=2, sq=3, sk=-5, M=NULL) == ALIGN
 
 
 def ps(L, x=P, n=1024, d=512, ldx=512, b=64, r=64, M=NULL, I=P, ws=P, wsb=1 << 30):

@@ -155,6 +155,147 @@ def test_exact_strided_operands():
     assert ok and worst < 1e-4
 
 
+# ---------------------------------- batches, causal masking, ragged last block
+BATCHED_SMALL = [
+    # (B, N, H, hd, block)
+    (1, 256, 2, 128, 64),
+    (2, 1000, 3, 64, 64),     # ragged: 15 whole blocks + 40 tokens
+    (3, 200, 2, 128, 32),     # ragged 32-row blocks
+    (1, 300, 1, 64, 128),     # ragged 128-row block spanning the tile's four waves
+    (2, 1, 1, 64, 64),        # one token: its only pair is excluded
+    (1, 65, 2, 64, 64),       # a last block of one token
+    (2, 1536, 4, 128, 64),    # 78 causal tiles: not a multiple of 8 (no XCD split)
+    (1, 2048, 4, 128, 64),    # 136 causal tiles: XCD split, groups of 8 query tiles
+]
+
+
+def rand_batch(seed, B, n, h, hd):
+    rng = np.random.default_rng(seed)
+    return (np.stack([synth.random_bf16(rng, (n, h * hd), 1.0) for _ in range(B)]),
+            np.stack([synth.random_bf16(rng, (n, h * hd), 1.0) for _ in range(B)]))
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+@pytest.mark.parametrize("shape", BATCHED_SMALL, ids=lambda s: "B%d_N%d_H%d_hd%d_b%d" % s)
+def test_scores_batched_small(shape, mode, causal):
+    B, n, h, hd, b = shape
+    say("batched scores", shape, mode, causal)
+    q, k = rand_batch(3000 + n + B, B, n, h, hd)
+    M_ref, I_ref = O.exact_block_scores_batched(q, k, h, hd, b, mode, causal=causal)
+    nb = -(-n // b)
+    M = torch.full((B, nb, nb), -1.0, device="cuda")        # every entry must be written
+    I, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), h, hd, b, mode, causal=causal, block_scores=M)
+    torch.cuda.synchronize()
+    Mg, Ig = M.cpu().numpy(), I.cpu().numpy()
+    assert (Mg >= 0).all()
+    okm, worstm = scores_close(Mg, M_ref)
+    ok, worst = scores_close(Ig, I_ref)
+    assert okm and ok and worstm < 1e-4 and worst < 1e-4, (worstm, worst)
+    if causal:
+        assert not Mg[:, np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]].any()
+
+
+def test_scores_batched_equals_single_call():
+    """One sequence, whole blocks, no mask: the same kernel as lemo_block_scores, bit for bit."""
+    q, k = rand_qk(41, 1024, 4, 128)
+    for mode in (O.REDUCE_PAPER, O.REDUCE_HEADMAX):
+        M1 = torch.empty((16, 16), device="cuda")
+        M2 = torch.empty((1, 16, 16), device="cuda")
+        I1, _ = lemo.lemo_block_scores(dev(q), dev(k), 4, 128, 64, mode, block_scores=M1)
+        I2, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), 4, 128, 64, mode, block_scores=M2)
+        assert torch.equal(I1, I2[0]) and torch.equal(M1, M2[0])
+
+
+def test_scores_batched_strided():
+    """Sequences inside a larger buffer: wide rows (ld > H*hd) and a gap
+    between sequences, NaN everywhere the call must not read."""
+    B, n, h, hd, b = 3, 320, 2, 64, 64
+    q, k = rand_batch(44, B, n, h, hd)
+    ld, gap_rows = 200, 5
+    buf_q = np.full((B, n + gap_rows, ld), 0x7FC0, np.uint16)
+    buf_k = np.full((B, n + gap_rows, ld), 0x7FC0, np.uint16)
+    buf_q[:, :n, :h * hd] = q
+    buf_k[:, :n, :h * hd] = k
+    qd, kd = dev(buf_q)[:, :n, :h * hd], dev(buf_k)[:, :n, :h * hd]
+    assert qd.stride() == ((n + gap_rows) * ld, ld, 1)
+    for causal in (False, True):
+        _, I_ref = O.exact_block_scores_batched(q, k, h, hd, b, O.REDUCE_HEADMAX, causal=causal)
+        I, _ = lemo.lemo_block_scores_batched(qd, kd, h, hd, b, O.REDUCE_HEADMAX, causal=causal)
+        ok, worst = scores_close(I.cpu().numpy(), I_ref)
+        assert ok and worst < 1e-4, (causal, worst)
+
+
+@pytest.mark.parametrize("n", [16384, 16384 - 40], ids=["N16384", "N16344_ragged"])
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+def test_causal_closed_form_full_size(mode, n):
+    """Q_i = a e and K_j = beta_j e in every head, 32 heads of 128, blocks of
+    64 (the 7B shape).  Causal: block pair (n, m) is a * max of beta_j over the
+    keys of block m that precede some query of block n, over sqrt(hd) (times
+    H for HEADMAX): all of block m below the diagonal, all but its last token
+    on it, nothing above.  So I[m] = (nb - 1 - m) * full[m] + diag[m]."""
+    h, hd, b = 32, 128, 64
+    nb = -(-n // b)
+    rng = np.random.default_rng(22)
+    a = 0.75
+    beta = synth.to_bf16_bits(np.abs(rng.standard_normal(n)).astype(np.float32) + 0.01)
+    bf = synth.bf16_bits_to_f32(beta).astype(np.float64)
+    q = np.zeros((n, h * hd), np.uint16)
+    k = np.zeros((n, h * hd), np.uint16)
+    q[:, 3::hd] = synth.to_bf16_bits(np.full((1,), a, np.float32))[0]
+    k[:, 3::hd] = beta[:, None]
+    c = a / math.sqrt(hd) * (h if mode == O.REDUCE_HEADMAX else 1)
+    full = np.array([bf[m * b:min((m + 1) * b, n)].max() for m in range(nb)]) * c
+    diag = np.array([bf[m * b:min((m + 1) * b, n) - 1].max() if min((m + 1) * b, n) - m * b > 1 else 0.0
+                     for m in range(nb)]) * c
+    expect = (nb - 1 - np.arange(nb)) * full + diag
+    M = torch.empty((1, nb, nb), device="cuda")
+    I, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), h, hd, b, mode, causal=True, block_scores=M)
+    ok, worst = scores_close(I.cpu().numpy()[0], expect, rel=1e-5)
+    assert ok, worst
+    Mg = M.cpu().numpy()[0]
+    assert not Mg[np.triu_indices(nb, 1)].any()
+    ok, worst = scores_close(Mg.diagonal(), diag, rel=1e-5)
+    assert ok, worst
+
+
+def test_causal_full_size_sampled():
+    """The 7B N=16K exact workload, causal, in the benchmark's launch
+    configuration: sampled block scores and whole columns from the oracle;
+    below the block diagonal the causal kernel repeats the full-attention
+    tiles, so those entries equal the full-attention call bit for bit."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("causal full size")
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, n_heads=w.n_heads, head_dim=w.head_dim,
+                         planted_frac=w.planted_frac, with_y=False, proj_device="cuda")
+    nb = w.n_blocks
+    rng = np.random.default_rng(6)
+    entries = [(0, 0), (nb - 1, nb - 1), (nb - 1, 0), (5, 200)] + \
+        [tuple(sorted(rng.integers(0, nb, 2))[::-1]) for _ in range(4)]
+    qd, kd = dev(L.q), dev(L.k)
+    lower = np.tril(np.ones((nb, nb), dtype=bool), -1)
+    for mode in (O.REDUCE_PAPER, O.REDUCE_HEADMAX):
+        M = torch.empty((1, nb, nb), device="cuda")
+        I, _ = lemo.lemo_block_scores_batched(qd, kd, w.n_heads, w.head_dim, w.block, mode, causal=True,
+                                              block_scores=M)
+        Mg, Ig = M.cpu().numpy()[0], I.cpu().numpy()[0]
+        for (r, c) in entries:
+            M_ref, _ = O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, mode, query_blocks=[r],
+                                            key_blocks=[c], causal=True)
+            ok, worst = scores_close([Mg[r, c]], M_ref[0])
+            assert ok and worst < 1e-4, (r, c, Mg[r, c], M_ref[0, 0])
+        for c in (nb - 1, 7):
+            I_ref, col = O.exact_column_score(L.q, L.k, w.n_heads, w.head_dim, w.block, mode, c, causal=True)
+            ok, worst = scores_close(Mg[:, c], col)
+            assert ok, (c, worst)
+            ok, worst = scores_close([Ig[c]], [I_ref])
+            assert ok and worst < 1e-4, (c, Ig[c], I_ref)
+        Mf = torch.empty((nb, nb), device="cuda")
+        lemo.lemo_block_scores(qd, kd, w.n_heads, w.head_dim, w.block, mode, block_scores=Mf)
+        assert np.array_equal(Mg[lower], Mf.cpu().numpy()[lower])
+        assert not Mg[np.triu_indices(nb, 1)].any()
+
+
 # ------------------------------------------------------------- predictor
 PRED_SMALL = [
     # (N, d, block, rank)
