@@ -48,8 +48,9 @@ def parse():
     return ap.parse_args()
 
 
-def load_traffic():
-    """HBM bytes per launch of the exact-score kernel from committed counter
+def load_traffic(causal=False):
+    """HBM bytes per launch of the exact-score kernel (PAPER head reduction;
+    the full-attention launch, or the causal one) from committed counter
     runs, only if they were taken on the current kernel source."""
     from contextual_token_sparsity_amd.rocprof_summary import kernel_source_hash
     try:
@@ -58,6 +59,8 @@ def load_traffic():
         return None
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
+    if causal:
+        return (rec.get("causal") or {}).get("hbm_bytes_per_launch")
     return rec.get("hbm_bytes_per_launch")
 
 
@@ -213,7 +216,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": load_traffic(),
+            "traffic": load_traffic() if mode == lemo.REDUCE_PAPER else None,
         },
         "stages_ms": stages,
         "n_kept_blocks": nk,
@@ -267,7 +270,8 @@ def causal_scores(q, k, N, H, hd, b, mode, stream, dev, reps=10):
     t = float(np.mean([e[0].elapsed_time(e[1]) for e in ev[3:]]))
     flops = 2.0 * hd * H * N * (N - 1) / 2
     tf = flops / (t * 1e-3) / 1e12
-    return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3)}
+    return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3),
+            "traffic": load_traffic(causal=True) if mode == lemo.REDUCE_PAPER else None}
 
 
 def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):
