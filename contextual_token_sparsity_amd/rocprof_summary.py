@@ -1,7 +1,8 @@
 """Turns rocprofv3 CSV output into the short summaries kept under profiles/.
 
-    # kernel durations (rocprofv3 --kernel-trace --stats ... -o trace)
-    python -m contextual_token_sparsity_amd.rocprof_summary trace STATS_CSV OUT_TXT "COMMAND"
+    # kernel durations (rocprofv3 --kernel-trace --stats ... -o trace); with the
+    # per-dispatch trace beside STATS_CSV, the exact-score launches in detail
+    python -m contextual_token_sparsity_amd.rocprof_summary trace STATS_CSV OUT_TXT "COMMAND" [TIMED_STEPS]
 
     # HBM bytes per launch of the exact-score kernel from two counter runs
     # (rocprofv3 --pmc FETCH_SIZE / --pmc WRITE_SIZE of `bench.py --copy-probe`)
@@ -33,7 +34,36 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def trace(stats_csv: str, out_txt: str, command: str) -> None:
+def _score_launches(trace_csv: str, timed_steps: int):
+    """Per-dispatch durations (us) of the benchmark's exact-score launches,
+    in dispatch order, from the kernel-trace CSV.  The full-attention
+    instantiation also serves the per-token predictor's one-head scores
+    (a few percent of the 32-head time): only dispatches of at least half
+    the longest one count.  The bench times `timed_steps` steps right
+    before its first causal launch."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    full = [(s, (e - s) / 1e3) for s, e, n in seq if SCORE_KERNEL in n]
+    causal = [(s, (e - s) / 1e3) for s, e, n in seq if CAUSAL_KERNEL in n]
+    if not full:
+        return []
+    top = max(d for _, d in full)
+    many = [(s, d) for s, d in full if d >= 0.5 * top]
+    first_causal = causal[0][0] if causal else None
+    timed = [d for s, d in many if first_causal is None or s < first_causal][-timed_steps:]
+    lines = ["", f"{SCORE_KERNEL}, 32-head launches only ({len(full) - len(many)} one-head launches of the "
+             f"per-token predictor left out): {len(many)} launches, avg {sum(d for _, d in many) / len(many):.1f} us "
+             "(includes the clock-settle launches)",
+             f"  the {len(timed)} launches just before the first causal launch (the bench's timed steps): "
+             f"avg {sum(timed) / max(len(timed), 1):.1f} us"]
+    if causal:
+        ds = [d for _, d in causal]
+        lines.append(f"{CAUSAL_KERNEL}: {len(ds)} launches, avg {sum(ds) / len(ds):.1f} us; "
+                     f"the last {min(10, len(ds))}: avg {sum(ds[-10:]) / len(ds[-10:]):.1f} us")
+    return lines
+
+
+def trace(stats_csv: str, out_txt: str, command: str, timed_steps: int = 10) -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "",
              f"{'kernel':<72} {'calls':>6} {'avg us':>10} {'min us':>10} {'max us':>10} {'% time':>7}"]
@@ -43,6 +73,9 @@ def trace(stats_csv: str, out_txt: str, command: str) -> None:
         lines.append(f"{short:<72} {r['Calls']:>6} {float(r['AverageNs']) / 1e3:>10.1f} "
                      f"{float(r['MinNs']) / 1e3:>10.1f} {float(r['MaxNs']) / 1e3:>10.1f} "
                      f"{float(r['Percentage']):>7.2f}")
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if trace_csv != stats_csv and os.path.exists(trace_csv):
+        lines += _score_launches(trace_csv, int(timed_steps))
     with open(out_txt, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -128,8 +161,8 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, command
 
 if __name__ == "__main__":
     cmd = sys.argv[1] if len(sys.argv) > 1 else ""
-    if cmd == "trace" and len(sys.argv) == 5:
-        trace(*sys.argv[2:5])
+    if cmd == "trace" and len(sys.argv) in (5, 6):
+        trace(*sys.argv[2:])
     elif cmd == "traffic" and len(sys.argv) == 7:
         traffic(*sys.argv[2:7])
     else:
