@@ -35,7 +35,11 @@ function that takes it):
     product is clamped at zero;
   * a block is kept when its score is >= the threshold; top-k ties go to the
     lower block index; NaN scores compare false and sort last;
-  * the residual add is the correctly rounded bf16 sum.
+  * the residual add is the correctly rounded bf16 sum, and the backward
+    recompute of the input the correctly rounded bf16 difference;
+  * the MLP block's token score sums over channels the largest magnitude of
+    the intermediate activation over the block's tokens; the SiLU-gated
+    activation is real-valued (not rounded) when formed from gate and up.
 
 Parity pins: every function here is pinned in tests/ by hand-computed
 examples (tests/golden), closed forms, invariants, brute force on tiny inputs
@@ -358,3 +362,65 @@ def scatter_residual(residual, block: int, kept, n_kept: int, y):
     for p, t in enumerate(rows):
         out[t] = bf16_round(bf16_decode(out[t]) + bf16_decode(y[p, :width]))
     return out
+
+
+def residual_recompute(residual_out, block: int, kept, n_kept: int, y):
+    """Backward recompute of a layer's input ([Jenga] 4.2.3, in-place
+    addition: during backpropagation the original input is recovered by
+    subtracting the block's output from the output embeddings).  For each kept
+    token the layer output (row p of y, in kept-block order) is subtracted from
+    that token's row; eliminated rows were never changed by the addition and
+    stay as they are.  Reading: the correctly rounded bf16 difference (formed
+    in float64, then rounded once).  When the forward addition rounded, this
+    is not the input bit for bit: per element it is off by at most half a bf16
+    spacing at the output value plus half a spacing at the result.
+    Returns new residual bits."""
+    out = np.array(residual_out, dtype=np.uint16, copy=True)
+    rows = kept_token_rows(kept, n_kept, block)
+    width = out.shape[1]
+    y = np.asarray(y)
+    for p, t in enumerate(rows):
+        out[t] = bf16_round(bf16_decode(out[t]) - bf16_decode(y[p, :width]))
+    return out
+
+
+# --------------------------------------------------------------------------
+def _block_channel_max_sum(mag, block: int) -> np.ndarray:
+    """I[m] = sum over channels c of max over the tokens i of block m of
+    mag[i, c]; the last block holds the N mod b remaining tokens."""
+    n = mag.shape[0]
+    nb = -(-n // block)
+    return np.array([mag[m * block:min((m + 1) * block, n)].max(axis=0).sum() for m in range(nb)])
+
+
+def mlp_block_scores(act, block: int) -> np.ndarray:
+    """Token-block informativeness from the MLP block's intermediate
+    activations ([Jenga] 4.2.1, "Extend to MLP Block": the output of the ReLU
+    layer, or for SiLU-gated MLPs the element-wise product of the gate
+    projection after SiLU and the up projection).
+
+    The pages state no aggregation.  Reading, mirroring Eq. 2 (keep the
+    magnitude that matters, take the maximum over the block's tokens) and the
+    Figure 6 caption (aggregate along the other axis):
+        I[m] = sum over channels c of max over tokens i in block m of |A[i, c]|.
+    A ReLU output is >= 0, so its magnitude is the value itself.
+
+    act: bf16 bits [N][w] (the activation tensor as the layer holds it).
+    Returns I float64 [ceil(N / b)]."""
+    return _block_channel_max_sum(np.abs(bf16_decode(act)), block)
+
+
+def silu_gated(gate, up) -> np.ndarray:
+    """SiLU(g) * u = g * u / (1 + e^-g) of bf16 gate and up projections,
+    real-valued (float64, not rounded)."""
+    g = bf16_decode(gate)
+    u = bf16_decode(up)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * u
+
+
+def mlp_block_scores_gated(gate, up, block: int) -> np.ndarray:
+    """mlp_block_scores of the SiLU-gated activation, formed from the gate
+    and up projections (bf16 bits [N][w] each) without rounding it to bf16
+    first (the activation is never stored)."""
+    return _block_channel_max_sum(np.abs(silu_gated(gate, up)), block)

@@ -603,6 +603,96 @@ def check_movement(o) -> list:
     return out
 
 
+def check_mlp_scores(o) -> list:
+    """MLP block scores: the hand example, a pure-Python brute force of the
+    plain and the SiLU-gated form (math.exp), closed forms of the gate, and
+    invariants (row order inside a block, channel order, sign, exact
+    doubling, a ragged last block)."""
+    out = []
+    e9 = golden()["E9_mlp_scores"]
+    a = f2bits(np.array(e9["act"]))
+    I = o.mlp_block_scores(a, e9["block"])
+    _fail(out, np.array_equal(I, np.array(e9["I"])), f"E9: {I.tolist()}")
+    I3 = o.mlp_block_scores(a[:3], e9["block"])
+    _fail(out, np.array_equal(I3, np.array(e9["I_first_three_rows"])), f"E9 ragged: {I3.tolist()}")
+    rng = np.random.default_rng(31)
+    for s in range(4):
+        n, w, b = int(rng.integers(1, 12)), int(rng.integers(1, 6)), int(rng.choice([2, 4]))
+        A = torch_bf16_bits(rng.standard_normal((n, w)).astype(np.float32))
+        G = torch_bf16_bits(3 * rng.standard_normal((n, w)).astype(np.float32))
+        Af, Gf = o.bf16_decode(A).tolist(), o.bf16_decode(G).tolist()
+        nb = (n + b - 1) // b
+        brute = [sum(max(abs(Af[i][c]) for i in range(m * b, min(m * b + b, n))) for c in range(w)) for m in range(nb)]
+        _fail(out, np.allclose(o.mlp_block_scores(A, b), brute, rtol=1e-14, atol=0), f"mlp brute force case {s}")
+        gated = [sum(max(abs(Gf[i][c] / (1.0 + math.exp(-Gf[i][c])) * Af[i][c]) for i in range(m * b, min(m * b + b, n)))
+                     for c in range(w)) for m in range(nb)]
+        _fail(out, np.allclose(o.mlp_block_scores_gated(G, A, b), gated, rtol=1e-13, atol=0),
+              f"gated brute force case {s}")
+    # invariants
+    n, w, b = 24, 10, 4
+    A = torch_bf16_bits(rng.standard_normal((n, w)).astype(np.float32))
+    I0 = o.mlp_block_scores(A, b)
+    perm_rows = np.concatenate([m * b + rng.permutation(b) for m in range(n // b)])
+    _fail(out, np.array_equal(o.mlp_block_scores(A[perm_rows], b), I0), "row order inside a block matters")
+    _fail(out, np.allclose(o.mlp_block_scores(A[:, rng.permutation(w)], b), I0, rtol=1e-14, atol=0),
+          "channel order matters")
+    _fail(out, np.array_equal(o.mlp_block_scores(A ^ np.uint16(0x8000), b), I0), "sign of the activation matters")
+    A2 = torch_bf16_bits(2 * o.bf16_decode(A).astype(np.float32))
+    _fail(out, np.allclose(o.mlp_block_scores(A2, b), 2 * I0, rtol=1e-14, atol=0), "doubling A does not double I")
+    _fail(out, np.array_equal(o.mlp_block_scores(A[:22], b)[:5], I0[:5]), "a ragged tail changes whole blocks")
+    # the gate: SiLU(0) = 0; SiLU(64) = 64 (1 + e^-64)^-1, within 2e-28 of 64; SiLU(-64) ~ -64 e^-64
+    zero = np.zeros((n, w), np.uint16)
+    _fail(out, not o.mlp_block_scores_gated(zero, A, b).any(), "SiLU(0) is not 0")
+    g64 = np.full((n, w), f2bits(np.array([64.0]))[0], np.uint16)
+    _fail(out, np.allclose(o.mlp_block_scores_gated(g64, A, b), 64 * I0, rtol=1e-15, atol=0), "SiLU(64) != 64")
+    gm64 = g64 | np.uint16(0x8000)
+    _fail(out, np.all(o.mlp_block_scores_gated(gm64, A, b) <= 64 * math.exp(-64) * I0 * (1 + 1e-12)),
+          "SiLU(-64) is not ~0")
+    return out
+
+
+def check_recompute(o) -> list:
+    """Backward recompute: the hand example (a forward tie that loses 2^-8),
+    torch's bf16 subtraction on random and structured pairs, dropped rows
+    untouched, y = 0 is the identity, exact forward additions come back
+    exactly, and every recomputed element lies within half a spacing at the
+    output plus half a spacing at the result of the original input."""
+    out = []
+    e = golden()["E10_recompute"]
+    x = f2bits(np.array(e["residual_in"]))
+    y = f2bits(np.array(e["y"]))
+    kept = np.array(e["kept"], np.int32)
+    fwd = o.scatter_residual(x, e["block"], kept, 1, y)
+    _fail(out, np.array_equal(o.bf16_decode(fwd), np.array(e["residual_out"])), f"E10 forward {fwd}")
+    rec = o.residual_recompute(fwd, e["block"], kept, 1, y)
+    _fail(out, np.array_equal(o.bf16_decode(rec), np.array(e["recomputed"])), f"E10 recompute {o.bf16_decode(rec)}")
+    rng = np.random.default_rng(8)
+    N, w, b = 64, 48, 8
+    x = torch_bf16_bits(rng.standard_normal((N, w)).astype(np.float32))
+    y = torch_bf16_bits((rng.standard_normal((N, w)) * np.exp2(rng.integers(-12, 4, (N, w)))).astype(np.float32))
+    kept = np.array([1, 4, 6, 7], np.int32)
+    rows = (kept[:, None] * b + np.arange(b)[None, :]).reshape(-1)
+    fwd = o.scatter_residual(x, b, kept, 4, y)
+    rec = o.residual_recompute(fwd, b, kept, 4, y)
+    # torch: bf16 - bf16 is the float32 difference rounded to nearest even
+    tr = (torch.from_numpy(o.bf16_decode(fwd[rows]).astype(np.float32)).bfloat16()
+          - torch.from_numpy(o.bf16_decode(y[:rows.size]).astype(np.float32)).bfloat16())
+    _fail(out, np.array_equal(rec[rows], tr.view(torch.int16).numpy().view(np.uint16)), "differs from torch's bf16 subtraction")
+    dropped = np.setdiff1d(np.arange(N), rows)
+    _fail(out, np.array_equal(rec[dropped], x[dropped]), "dropped rows changed")
+    _fail(out, np.array_equal(o.residual_recompute(x, b, kept, 4, np.zeros_like(y)), x), "y = 0 is not the identity")
+
+    def spacing(v):
+        _, ex = np.frexp(np.abs(v))
+        return np.ldexp(1.0, np.maximum(ex - 8, -133))
+    xv, fv, rv = o.bf16_decode(x[rows]), o.bf16_decode(fwd[rows]), o.bf16_decode(rec[rows])
+    _fail(out, np.all(np.abs(rv - xv) <= 0.5 * spacing(fv) + 0.5 * spacing(rv)), "recompute outside its bound")
+    _fail(out, np.any(rv != xv), "no rounding loss on random data (test too weak)")
+    exact = o.bf16_decode(fwd[rows]) == xv + o.bf16_decode(y[:rows.size])
+    _fail(out, np.array_equal(rv[exact], xv[exact]) and exact.any(), "exact additions do not come back exactly")
+    return out
+
+
 ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
               check_exact_closed_form, check_exact_invariants, check_predictor, check_token_predictor,
-              check_select, check_movement, check_fused_movement]
+              check_select, check_movement, check_fused_movement, check_mlp_scores, check_recompute]

@@ -75,8 +75,21 @@ MUTATIONS = [
      "return ((kept[:, None] + 1) * block + np.arange(block)[None, :]).reshape(-1) % 6", [P.check_movement]),
     ("pad_not_zeroed", "        dst[p, :width] = 0\n    return dst, n_pad > cap\n\n\ndef linear_bf16",
      "        pass\n    return dst, n_pad > cap\n\n\ndef linear_bf16", [P.check_movement]),
-    ("scatter_into_dense_rows", "for p, t in enumerate(rows):", "for p, t in enumerate(range(rows.size)):",
-     [P.check_movement]),
+    ("scatter_into_dense_rows", "for p, t in enumerate(rows):\n        out[t] = bf16_round(bf16_decode(out[t]) +",
+     "for p, t in enumerate(range(rows.size)):\n        out[t] = bf16_round(bf16_decode(out[t]) +", [P.check_movement]),
+    ("recompute_adds", "bf16_decode(out[t]) - bf16_decode(y[p, :width])", "bf16_decode(out[t]) + bf16_decode(y[p, :width])",
+     [P.check_recompute]),
+    ("recompute_into_dense_rows", "for p, t in enumerate(rows):\n        out[t] = bf16_round(bf16_decode(out[t]) -",
+     "for p, t in enumerate(range(rows.size)):\n        out[t] = bf16_round(bf16_decode(out[t]) -", [P.check_recompute]),
+    ("recompute_y_misaligned", "bf16_decode(out[t]) - bf16_decode(y[p, :width])", "bf16_decode(out[t]) - bf16_decode(y[t, :width])",
+     [P.check_recompute]),
+    ("mlp_no_magnitude", "_block_channel_max_sum(np.abs(bf16_decode(act)), block)", "_block_channel_max_sum(bf16_decode(act), block)",
+     [P.check_mlp_scores]),
+    ("mlp_mean_not_max", ".max(axis=0).sum() for m in range(nb)", ".mean(axis=0).sum() for m in range(nb)", [P.check_mlp_scores]),
+    ("mlp_ragged_block_dropped", "nb = -(-n // block)\n    return np.array([mag", "nb = n // block\n    return np.array([mag",
+     [P.check_mlp_scores]),
+    ("silu_wrong_sign", "g / (1.0 + np.exp(-g)) * u", "g / (1.0 + np.exp(g)) * u", [P.check_mlp_scores]),
+    ("gated_uses_gate_twice", "g / (1.0 + np.exp(-g)) * u", "g / (1.0 + np.exp(-g)) * g", [P.check_mlp_scores]),
 ]
 
 
