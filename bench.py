@@ -233,6 +233,8 @@ def main():
         "clock_settle_steps": settle_steps,
     }
     out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
+    out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
+    out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
     if args.copy_probe:
@@ -272,6 +274,45 @@ def causal_scores(q, k, N, H, hd, b, mode, stream, dev, reps=10):
     tf = flops / (t * 1e-3) / 1e12
     return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3),
             "traffic": load_traffic(causal=True) if mode == lemo.REDUCE_PAPER else None}
+
+
+def _mean_ms(fn, stream, reps=10, warm=3):
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps + warm)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in ev[warm:]]))
+
+
+def mlp_scores(act, N, wm, b, stream, dev):
+    """MLP-block token scores on the layer's MLP activation [N][wm] (one pass
+    over it), and the SiLU-gated form from a gate and an up projection of the
+    same shape (two passes' worth of bytes).  Algorithmic bytes: every
+    activation element read once, 2 B each."""
+    import torch
+    from contextual_token_sparsity_amd import lemo, synth
+    I = torch.empty(-(-N // b), dtype=torch.float32, device=dev)
+    ws = torch.empty(lemo.lemo_mlp_block_scores_workspace(N, wm, b), dtype=torch.uint8, device=dev)
+    upj = torch.from_numpy(synth.random_bf16(np.random.default_rng(99), (N, wm)).view(np.int16)).to(dev)
+    t = _mean_ms(lambda: lemo.lemo_mlp_block_scores(act, b, scores=I, workspace=ws), stream)
+    tg = _mean_ms(lambda: lemo.lemo_mlp_block_scores_gated(act, upj, b, scores=I, workspace=ws), stream)
+    by = 2.0 * N * wm
+    return {"ms": t, "GBps": by / (t * 1e-3) / 1e9, "frac": by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "gated_ms": tg, "gated_GBps": 2 * by / (tg * 1e-3) / 1e9,
+            "gated_frac": 2 * by / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def recompute(resid, y, kept, n_kept, nk, d, b, stream):
+    """Backward recompute of the layer input on the step's mask (the kept
+    rows of the residual minus the layer output), the mirror of the in-place
+    addition: 3 w 2 B per kept row."""
+    from contextual_token_sparsity_amd import lemo
+    t = _mean_ms(lambda: lemo.lemo_residual_recompute(resid, b, kept, n_kept, y), stream)
+    by = 3.0 * nk * b * d * 2
+    return {"ms": t, "GBps": by / (t * 1e-3) / 1e9, "frac": by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblemo.so")
-SOURCES = ["abi.hip", "block_scores.hip", "predict.hip", "token.hip", "select.hip", "movement.hip", "fused.hip"]
+SOURCES = ["abi.hip", "block_scores.hip", "predict.hip", "token.hip", "select.hip", "movement.hip", "fused.hip",
+           "mlp.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

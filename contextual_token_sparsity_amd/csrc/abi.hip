@@ -268,6 +268,62 @@ lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, 
                        "lemo_scatter_residual launch");
 }
 
+lemo_status lemo_residual_recompute(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                   const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y, int ld_y,
+                                   int32_t* dev_status, void* stream) {
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
+  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
+  REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
+  lemo_status st;
+  if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
+  if ((st = check_rows(y, ld_y, width, "y")) != LEMO_OK) return st;
+  return device_status(lemo_launch_scatter(residual, n_tokens, width, ld_res, block, kept_blocks, n_kept, y, ld_y,
+                                           dev_status, static_cast<hipStream_t>(stream), true),
+                       "lemo_residual_recompute launch");
+}
+
+size_t lemo_mlp_block_scores_workspace(int n_tokens, int width, int block) {
+  if (n_tokens <= 0 || width <= 0 || block <= 0) return 0;
+  const size_t nb = (size_t)((n_tokens + block - 1) / block);
+  return lemo_align256(nb * lemo_mlp_chunks(width) * sizeof(float));
+}
+
+static lemo_status mlp_scores(const char* fn, const lemo_bf16* act, int ld_act, const lemo_bf16* up, int ld_up,
+                              int n_tokens, int width, int block, float* scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  REQUIRE(scores != nullptr, LEMO_ERR_INVALID_ARG, "scores is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
+  REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
+  REQUIRE(lemo_mlp_chunks(width) <= 65535, LEMO_ERR_UNSUPPORTED, "width %d too large", width);
+  lemo_status st;
+  if ((st = check_rows(act, ld_act, width, up ? "gate" : "act")) != LEMO_OK) return st;
+  if (up && (st = check_rows(up, ld_up, width, "up")) != LEMO_OK) return st;
+  const size_t need = lemo_mlp_block_scores_workspace(n_tokens, width, block);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+          "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned16(workspace), LEMO_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  return device_status(lemo_launch_mlp_scores(act, ld_act, up, ld_up, n_tokens, width, block, scores, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                       fn);
+}
+
+lemo_status lemo_mlp_block_scores(const lemo_bf16* act, int n_tokens, int width, int ld_act, int block,
+                                  float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  return mlp_scores("lemo_mlp_block_scores launch", act, ld_act, nullptr, 0, n_tokens, width, block, scores,
+                    workspace, workspace_bytes, stream);
+}
+
+lemo_status lemo_mlp_block_scores_gated(const lemo_bf16* gate, const lemo_bf16* up, int n_tokens, int width,
+                                        int ld_gate, int ld_up, int block, float* scores, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  REQUIRE(up != nullptr, LEMO_ERR_INVALID_ARG, "up is NULL");
+  return mlp_scores("lemo_mlp_block_scores_gated launch", gate, ld_gate, up, ld_up, n_tokens, width, block, scores,
+                    workspace, workspace_bytes, stream);
+}
+
 lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int ld_x, int block,
                                const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* weight,
                                int d_out, int ld_w, lemo_bf16* y, int ld_y, int cap_rows, int pad_multiple,

@@ -74,9 +74,17 @@ hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int 
                               const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst,
                               int cap_rows, int pad_multiple, int32_t* dev_status, hipStream_t stream);
 
+// subtract: the backward recompute res -= y instead of res += y
 hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block,
                                const int32_t* kept, const int32_t* n_kept, const uint16_t* y, int ld_y,
-                               int32_t* dev_status, hipStream_t stream);
+                               int32_t* dev_status, hipStream_t stream, bool subtract = false);
+
+// MLP-block scores: act [n_tokens][ld_act]; with `up` non-NULL, act is the
+// gate projection and the activation is SiLU(act) * up.  Workspace: fp32
+// partials [ceil(n_tokens / block)][lemo_mlp_chunks(width)].
+int lemo_mlp_chunks(int width);
+hipError_t lemo_launch_mlp_scores(const uint16_t* act, int ld_act, const uint16_t* up, int ld_up, int n_tokens,
+                                  int width, int block, float* scores, void* workspace, hipStream_t stream);
 
 hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream, int n_batch = 1);
 

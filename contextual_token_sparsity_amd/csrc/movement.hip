@@ -2,6 +2,8 @@
 // "selective load" reads the kept tokens from their original rows, and
 // "in-place addition" adds the layer output of each kept token back into its
 // original row, so eliminated tokens are never copied, padded or touched.
+// In backpropagation the same rows give the layer's input back by
+// subtracting the layer output (the recompute variant of the scatter).
 //
 // Both kernels are HBM-bound row copies: a workgroup of 256 threads moves a
 // 4 KiB column stripe (256 x 16 bytes) of a row per step, rows are strided
@@ -30,6 +32,11 @@ __device__ __forceinline__ void store_stream(uint16_t* p, uint4 v) {
   __builtin_nontemporal_store(w, reinterpret_cast<lemo_u32x4*>(p));
 }
 
+// a + b (SUB: a - b) on 8 bf16 pairs: fp32 add, round to nearest even.  Two
+// bf16 values add or subtract exactly in fp32 unless one is below 2^-16 of
+// the other, where the rounded result is the larger one either way, so this
+// is the correctly rounded bf16 sum or difference.
+template <bool SUB>
 __device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b) {
   const uint32_t* pa = &a.x;
   const uint32_t* pb = &b.x;
@@ -37,8 +44,9 @@ __device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b) {
   uint32_t* po = &o.x;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = lemo_bf16_to_f32(pa[j] & 0xffffu) + lemo_bf16_to_f32(pb[j] & 0xffffu);
-    const float hi = lemo_bf16_to_f32(pa[j] >> 16) + lemo_bf16_to_f32(pb[j] >> 16);
+    const float blo = lemo_bf16_to_f32(pb[j] & 0xffffu), bhi = lemo_bf16_to_f32(pb[j] >> 16);
+    const float lo = lemo_bf16_to_f32(pa[j] & 0xffffu) + (SUB ? -blo : blo);
+    const float hi = lemo_bf16_to_f32(pa[j] >> 16) + (SUB ? -bhi : bhi);
     po[j] = lemo_f32_to_bf16(lo) | (lemo_f32_to_bf16(hi) << 16);
   }
   return o;
@@ -96,6 +104,8 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
   }
 }
 
+// res[token(p)] = res[token(p)] + y[p] for the kept rows p (SUB: minus).
+template <bool SUB>
 __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res, int n_tokens, int width, int ld_res,
                                                       int block, const int32_t* __restrict__ kept,
                                                       const int32_t* __restrict__ n_kept_p,
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
 #pragma unroll
     for (int u = 0; u < kUnrollScatter; ++u) {
       if (tok[u] >= 0) {
-        store_stream(res + (size_t)tok[u] * ld_res + ch * 8, add_bf16x8(r[u], a[u]));
+        store_stream(res + (size_t)tok[u] * ld_res + ch * 8, add_bf16x8<SUB>(r[u], a[u]));
       } else if (tok[u] == -1 && status) {
         atomicOr(status, LEMO_DEV_BAD_KEPT);
       }
@@ -156,8 +166,12 @@ hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int 
 
 hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block, const int32_t* kept,
                                const int32_t* n_kept, const uint16_t* y, int ld_y, int32_t* dev_status,
-                               hipStream_t stream) {
-  hipLaunchKernelGGL(k_scatter, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens, width, ld_res,
-                     block, kept, n_kept, y, ld_y, dev_status);
+                               hipStream_t stream, bool subtract) {
+  if (subtract)
+    hipLaunchKernelGGL(k_scatter<true>, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens, width,
+                       ld_res, block, kept, n_kept, y, ld_y, dev_status);
+  else
+    hipLaunchKernelGGL(k_scatter<false>, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens, width,
+                       ld_res, block, kept, n_kept, y, ld_y, dev_status);
   return hipGetLastError();
 }

@@ -37,6 +37,10 @@ _SIGS = {
     "lemo_select_mask": (_i, [_vp, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_residual_recompute": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_mlp_block_scores_workspace": (_sz, [_i, _i, _i]),
+    "lemo_mlp_block_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "lemo_mlp_block_scores_gated": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "lemo_gather_linear": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_linear_scatter": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "lemo_status_string": (ctypes.c_char_p, [_i]),
@@ -251,6 +255,53 @@ def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: i
                                      _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
     _check(st, "lemo_scatter_residual")
     return residual
+
+
+def lemo_residual_recompute(residual, block: int, kept_blocks, n_kept, y, width: int = None, n_tokens: int = None,
+                            dev_status=None):
+    """Backward recompute: subtracts y's rows from the kept rows of residual, in place."""
+    _bf16(residual), _bf16(y)
+    w = residual.shape[1] if width is None else width
+    n = residual.shape[0] if n_tokens is None else n_tokens
+    st = lib().lemo_residual_recompute(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
+                                       _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
+    _check(st, "lemo_residual_recompute")
+    return residual
+
+
+def lemo_mlp_block_scores_workspace(n_tokens: int, width: int, block: int) -> int:
+    return lib().lemo_mlp_block_scores_workspace(n_tokens, width, block)
+
+
+def _mlp_out(a, block, width, scores, workspace):
+    n = a.shape[0]
+    w = a.shape[1] if width is None else width
+    if scores is None:
+        scores = torch.empty(-(-n // block), dtype=torch.float32, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(max(lemo_mlp_block_scores_workspace(n, w, block), 1), dtype=torch.uint8,
+                                device=a.device)
+    return n, w, scores, workspace
+
+
+def lemo_mlp_block_scores(act, block: int, width: int = None, scores=None, workspace=None):
+    """MLP-block token scores from an activation [N][w]; returns scores [ceil(N / block)] fp32."""
+    _bf16(act)
+    n, w, scores, workspace = _mlp_out(act, block, width, scores, workspace)
+    st = lib().lemo_mlp_block_scores(_ptr(act), n, w, _ld(act), block, _ptr(scores), _ptr(workspace),
+                                     workspace.numel(), _stream(act.device))
+    _check(st, "lemo_mlp_block_scores")
+    return scores
+
+
+def lemo_mlp_block_scores_gated(gate, up, block: int, width: int = None, scores=None, workspace=None):
+    """MLP-block token scores of SiLU(gate) * up; returns scores [ceil(N / block)] fp32."""
+    _bf16(gate), _bf16(up)
+    n, w, scores, workspace = _mlp_out(gate, block, width, scores, workspace)
+    st = lib().lemo_mlp_block_scores_gated(_ptr(gate), _ptr(up), n, w, _ld(gate), _ld(up), block, _ptr(scores),
+                                           _ptr(workspace), workspace.numel(), _stream(gate.device))
+    _check(st, "lemo_mlp_block_scores_gated")
+    return scores
 
 
 def lemo_gather_linear(x, block: int, kept_blocks, n_kept, weight, y, pad_multiple: int = 1, d_in: int = None,

@@ -10,6 +10,9 @@
  *   threshold / compact  lemo_select_mask       (pages: layer threshold, Alg. 1 step 1)
  *   selective load       lemo_gather_pad        (pages: permutation-free movement)
  *   in-place addition    lemo_scatter_residual  (pages: permutation-free movement)
+ *     its backward recompute: lemo_residual_recompute
+ *   MLP-block scores     lemo_mlp_block_scores, lemo_mlp_block_scores_gated
+ *                        (pages: extension of token elimination to the MLP block)
  *   movement fused into the layer's products: lemo_gather_linear, lemo_linear_scatter
  * "The pages" are "Jenga: Enhancing LLM Long-Context Fine-tuning with
  * Contextual Token Sparsity" (USENIX ATC'25; summary page, section 4.2) and
@@ -37,7 +40,8 @@
  *  - Pointers to bf16 matrices must be 16-byte aligned and their ld a
  *    multiple of 8 elements (128-bit row access).
  *  - Inputs and outputs of one call must not overlap, except the residual of
- *    lemo_scatter_residual, which is updated in place by design.
+ *    lemo_scatter_residual, lemo_residual_recompute and lemo_linear_scatter,
+ *    which is updated in place by design.
  *  - Same inputs on the same device give bitwise-identical outputs (no
  *    floating-point atomics anywhere).
  *  - Calls are thread-safe; calls that share output buffers on one stream
@@ -290,6 +294,53 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
 lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
                                   const int32_t* kept_blocks, const int32_t* n_kept,
                                   const lemo_bf16* y, int ld_y, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward recompute of a layer's input (Jenga 4.2.3, in-place addition:
+ * during backpropagation the original input is recovered by subtracting the
+ * block's output from the output embeddings), so the forward pass need not
+ * keep a copy of the residual stream.
+ *
+ *  residual[t] = bf16_rne(fp32(residual[t]) - fp32(y[p])) for the same kept
+ *  rows p and tokens t as lemo_scatter_residual; eliminated rows, which the
+ *  addition never changed, are left bit-identical.  When the forward
+ *  addition rounded, the result is not the input bit for bit: each element
+ *  is within half a bf16 spacing at the output value plus half a spacing at
+ *  the result.  Arguments, errors and dev_status as lemo_scatter_residual.
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_residual_recompute(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                   const int32_t* kept_blocks, const int32_t* n_kept,
+                                   const lemo_bf16* y, int ld_y, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token-block scores from the MLP block (Jenga 4.2.1, "Extend to MLP
+ * Block": the intermediate activation rates the tokens -- the ReLU output,
+ * or for SiLU-gated MLPs SiLU(gate projection) * up projection).  The pages
+ * state no aggregation; as Eq. 2 takes a block maximum and Figure 6 sums
+ * along the other axis:
+ *   I[m] = sum over channels c of max over tokens i in block m of |A[i][c]|.
+ * The last of ceil(n_tokens / block) blocks holds the remaining tokens when
+ * n_tokens is not a multiple of block.
+ *
+ *  act            bf16 [n_tokens][ld_act], width channels used (a ReLU
+ *                 output, or any activation: magnitudes are taken).
+ *  gate, up       (gated call) bf16 [n_tokens][ld] pre-activation gate and
+ *                 up projections; A = SiLU(gate) * up is formed in fp32 in
+ *                 registers (SiLU(g) = g / (1 + e^-g)), not rounded and
+ *                 never stored.
+ *  width          multiple of 8.   block: any positive size.
+ *  scores         fp32 [ceil(n_tokens / block)] output I.
+ *  workspace      lemo_mlp_block_scores_workspace() bytes (per-chunk partial
+ *                 sums), 16-byte aligned.
+ * Errors: INVALID_ARG (NULL, sizes, ld < width), ALIGNMENT (pointers, ld,
+ * width), WORKSPACE.  Non-finite activations give unspecified scores.
+ * ------------------------------------------------------------------------ */
+size_t lemo_mlp_block_scores_workspace(int n_tokens, int width, int block);
+lemo_status lemo_mlp_block_scores(const lemo_bf16* act, int n_tokens, int width, int ld_act, int block,
+                                  float* scores, void* workspace, size_t workspace_bytes, void* stream);
+lemo_status lemo_mlp_block_scores_gated(const lemo_bf16* gate, const lemo_bf16* up, int n_tokens, int width,
+                                        int ld_gate, int ld_up, int block, float* scores, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 const char* lemo_status_string(lemo_status s);
 const char* lemo_last_error(void); /* thread-local detail of the last non-OK return */

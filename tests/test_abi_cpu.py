@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 16
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
 
@@ -202,3 +202,51 @@ def sc(L, res=P, n=1024, w=512, ldr=512, b=64, kept=P, nk=P, y=P, ldy=512):
 ])
 def test_scatter_rejects(L, kw, status):
     assert sc(L, **kw) == status
+
+
+def rc(L, res=P, n=1024, w=64, ldr=64, b=64, kept=P, nk=P, y=P, ldy=64):
+    return L.lemo_residual_recompute(res, n, w, ldr, b, kept, nk, y, ldy, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID), (dict(res=NULL), INVALID), (dict(y=NULL), INVALID),
+    (dict(n=0), INVALID), (dict(n=1000), INVALID), (dict(ldr=32), INVALID),
+    (dict(w=60, ldr=64, ldy=64), ALIGN), (dict(res=P2), ALIGN), (dict(ldy=68), ALIGN),
+])
+def test_residual_recompute_rejects(L, kw, status):
+    assert rc(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def test_mlp_workspace_query(L):
+    # 16384 tokens in blocks of 64 -> 256 blocks; 11008 channels -> 6 chunks of 2048
+    assert L.lemo_mlp_block_scores_workspace(16384, 11008, 64) == 256 * 6 * 4
+    assert L.lemo_mlp_block_scores_workspace(1000, 200, 64) == 256      # 16 x 1 x 4 B, rounded up to 256
+    assert L.lemo_mlp_block_scores_workspace(0, 200, 64) == 0
+
+
+def ms(L, a=P, n=1000, w=200, lda=200, b=64, I=P, ws=P, wsb=1 << 20, up=None, ldu=200):
+    if up is None:
+        return L.lemo_mlp_block_scores(a, n, w, lda, b, I, ws, wsb, NULL)
+    return L.lemo_mlp_block_scores_gated(a, up, n, w, lda, ldu, b, I, ws, wsb, NULL)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=NULL), INVALID), (dict(a=NULL), INVALID), (dict(n=0), INVALID), (dict(b=0), INVALID),
+    (dict(w=0), INVALID), (dict(lda=192), INVALID),
+    (dict(w=196, lda=200), ALIGN), (dict(a=P2), ALIGN), (dict(lda=204), ALIGN), (dict(ws=P2), ALIGN),
+    (dict(ws=NULL), WS), (dict(wsb=100), WS),
+])
+def test_mlp_scores_rejects(L, kw, status, gated):
+    kw = dict(kw)
+    if gated:
+        kw.setdefault("up", P)
+    assert ms(L, **kw) == status
+    assert lemo.lemo_last_error()
+
+
+def test_mlp_gated_rejects_bad_up(L):
+    assert L.lemo_mlp_block_scores_gated(P, NULL, 1000, 200, 200, 200, 64, P, P, 1 << 20, NULL) == INVALID
+    assert ms(L, up=P2) == ALIGN
+    assert ms(L, up=P, ldu=100) == INVALID

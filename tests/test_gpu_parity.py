@@ -477,6 +477,111 @@ def test_gather_scatter(case):
     assert int(status.item()) == 0
 
 
+@pytest.mark.parametrize("case", MOVE, ids=lambda c: "N%d_w%d_b%d_keep%.2f" % (c[0], c[1], c[4], c[5]))
+def test_residual_recompute(case):
+    """Backward recompute, bit for bit against the oracle on an independent
+    random residual; then the forward addition followed by the recompute on
+    the GPU comes back within the rounding bound of the input (and exactly
+    where the addition was exact)."""
+    n, w, lds, ldd, b, frac, pad, extra = case
+    say("recompute", case)
+    rng = np.random.default_rng(n + w + 7)
+    nb = n // b
+    kept = _kept_from_mask(rng, nb, frac)
+    nk = kept.size
+    R = nk * b
+    res = synth.random_bf16(rng, (n, w))
+    y = synth.random_bf16(rng, (max(R, 1), w), 0.05)
+    kept_d = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    kept_d[:nk] = torch.from_numpy(kept).cuda()
+    nk_d = torch.tensor([nk], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ref = O.residual_recompute(res, b, kept, nk, y)
+    resd = padded(res, lds, 0x4321)
+    yd = padded(y, ldd, 0x7FC0)
+    lemo.lemo_residual_recompute(resd[:, :w], b, kept_d, nk_d, yd[:, :w], dev_status=status)
+    got = host_bits(resd)
+    assert np.array_equal(got[:, :w], ref)
+    assert np.all(got[:, w:] == 0x4321) and int(status.item()) == 0
+    # round trip on the GPU: x -> x + y -> (x + y) - y
+    xd = padded(res, lds, 0x4321)
+    lemo.lemo_scatter_residual(xd[:, :w], b, kept_d, nk_d, yd[:, :w])
+    fwd = host_bits(xd)[:, :w]
+    lemo.lemo_residual_recompute(xd[:, :w], b, kept_d, nk_d, yd[:, :w])
+    back = host_bits(xd)[:, :w]
+    assert np.array_equal(back, O.residual_recompute(O.scatter_residual(res, b, kept, nk, y), b, kept, nk, y))
+    rows = (kept[:, None] * b + np.arange(b)[None, :]).reshape(-1)
+    xv, fv, bv = (O.bf16_decode(a[rows]) for a in (res, fwd, back))
+    spacing = lambda v: np.ldexp(1.0, np.maximum(np.frexp(np.abs(v))[1] - 8, -133))
+    assert np.all(np.abs(bv - xv) <= 0.5 * spacing(fv) + 0.5 * spacing(bv))
+    exact = fv == xv + O.bf16_decode(y[:rows.size])
+    assert np.array_equal(bv[exact], xv[exact])
+    dropped = np.setdiff1d(np.arange(n), rows)
+    assert np.array_equal(back[dropped], res[dropped])
+
+
+MLP_SMALL = [
+    # (N, width, block, ld)
+    (256, 64, 64, 64),
+    (1000, 200, 64, 208),       # ragged last block (40 tokens), ld > width
+    (200, 2056, 32, 2056),      # two channel chunks, the second 8 wide; ragged (8 tokens)
+    (1, 8, 64, 8),              # one token
+    (130, 11008, 64, 11008),    # the MLP width of the 7B shape; a 2-token last block
+    (4096, 4104, 128, 4104),
+    (96, 16, 1, 16),            # blocks of one token
+]
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["act", "gated"])
+@pytest.mark.parametrize("case", MLP_SMALL, ids=lambda c: "N%d_w%d_b%d" % c[:3])
+def test_mlp_scores_small(case, gated):
+    n, w, b, ld = case
+    say("mlp scores", case, gated)
+    rng = np.random.default_rng(n + w + b)
+    a = synth.random_bf16(rng, (n, w))
+    if gated:
+        u = synth.random_bf16(rng, (n, w))
+        ref = O.mlp_block_scores_gated(a, u, b)
+        got = lemo.lemo_mlp_block_scores_gated(padded(a, ld, 0x7FC0)[:, :w], padded(u, ld, 0x7FC0)[:, :w], b)
+    else:
+        ref = O.mlp_block_scores(a, b)
+        got = lemo.lemo_mlp_block_scores(padded(a, ld, 0x7FC0)[:, :w], b)
+    got = got.cpu().numpy()
+    assert got.shape == ref.shape
+    ok, worst = scores_close(got, ref)
+    assert ok and worst < 1e-5, worst
+
+
+def test_mlp_scores_relu_output_and_determinism():
+    """A ReLU output (non-negative, many zeros) at the 7B shape's width; two
+    calls give the same bits."""
+    rng = np.random.default_rng(12)
+    a = synth.random_bf16(rng, (2048, 11008))
+    a[(a & 0x8000) != 0] = 0                      # ReLU: negatives to +0
+    ref = O.mlp_block_scores(a, 64)
+    ad = dev(a)
+    g1 = lemo.lemo_mlp_block_scores(ad, 64).cpu().numpy()
+    g2 = lemo.lemo_mlp_block_scores(ad, 64).cpu().numpy()
+    assert g1.tobytes() == g2.tobytes()
+    ok, worst = scores_close(g1, ref)
+    assert ok and worst < 1e-5, worst
+
+
+def test_mlp_scores_full_size():
+    """The 7B N=16K MLP activation (16384 x 11008) in the benchmark's launch
+    configuration, against the full oracle, plain and gated."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("mlp scores full size")
+    rng = np.random.default_rng(13)
+    a = synth.random_bf16(rng, (w.n_tokens, w.mlp_width))
+    ok, worst = scores_close(lemo.lemo_mlp_block_scores(dev(a), w.block).cpu().numpy(), O.mlp_block_scores(a, w.block))
+    assert ok and worst < 1e-5, worst
+    u = synth.random_bf16(rng, (w.n_tokens, w.mlp_width))
+    ok, worst = scores_close(lemo.lemo_mlp_block_scores_gated(dev(a), dev(u), w.block).cpu().numpy(),
+                             O.mlp_block_scores_gated(a, u, w.block))
+    assert ok and worst < 1e-5, worst
+
+
 def test_gather_capacity_overflow():
     n, w, b = 512, 64, 16
     rng = np.random.default_rng(2)
