@@ -20,12 +20,14 @@
 //   ahead of the MFMAs.
 //
 // The score tile never leaves registers:
-//   PAPER   (heads first, then block max): each head's MFMA chain starts from
-//           the running sum over heads of max(0, S^h) as its C operand, so
-//           after the chain acc = sum + S^h, and sum = max(acc, sum) is the
-//           update.  sum >= 0 always, and for a non-negative float the bit
-//           pattern orders like a signed integer while a negative float is a
-//           negative integer: the update is one v_max_i32 per element.
+//   PAPER   (heads first, then block max): each head's MFMA chain starts
+//           from 0 and the head is folded in as sum += max(0, S^h).  For a
+//           non-negative float the bit pattern orders like a signed integer
+//           while a negative float is a negative integer, so the clamp is one
+//           v_max_i32 against 0.  (Starting the chain from the running sum
+//           instead, with sum = max(sum + S^h, sum), needs one VALU op less
+//           but makes the compiler copy the 64 sum registers into the
+//           accumulators at every head: 3-10 % slower.)
 //   HEADMAX (per-head block max): the head's accumulators are reduced with
 //           v_max_i32 starting from 0, which yields max(0, block max) (the
 //           clamp is free for the same reason), then across lanes; the clamped
@@ -150,10 +152,17 @@ __device__ __forceinline__ void tri_tile_of(int logical, int ntq, int& tq, int& 
   }
 }
 
-template <int HD, int MODE, int BLK, bool CAUSAL>
+// Which pairs a launch must exclude.  kMaskDiag: only i == j, all a launch
+// needs when N is a multiple of the block size (rows past N in the last tile
+// then form whole blocks that are never written); kMaskRagged: also rows past
+// N inside the last block; kMaskCausal: every j >= i and rows past N.
+enum { kMaskDiag = 0, kMaskRagged = 1, kMaskCausal = 2 };
+
+template <int HD, int MODE, int BLK, int MASK>
 __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int n_heads, int ldq,
     int ldk, long long bsq, long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr int kCPH = HD / kChunk;                      // chunks per head
   constexpr int kParts = (MODE == 1 && BLK == 128) ? kMaxHeadsHeadmax : 1;
   __shared__ float part[kWaves][kParts];                 // HEADMAX, 128-row blocks: per-head wave maxima
@@ -179,7 +188,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   const int l32 = lane & 31, hi = lane >> 5;
   // does this wave's 64 x 64 square hold a pair that takes no part?
   const int qlo = q0 + wq * 64, klo = k0 + wk * 64;
-  const bool mask_wave = (CAUSAL ? klo >= qlo : klo == qlo) || qlo + 64 > n_tokens || klo + 64 > n_tokens;
+  const bool mask_wave = MASK == kMaskDiag
+                             ? klo == qlo
+                             : (CAUSAL ? klo >= qlo : klo == qlo) || qlo + 64 > n_tokens || klo + 64 > n_tokens;
   const uint32_t lds0 = (uint32_t)(uintptr_t)g_stage;
 
   // ---- per-lane DMA byte offsets: instruction i of this wave fills LDS
@@ -240,6 +251,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     }
   };
 
+  // the exclusions of sub-tile (a, b) of a masked wave; with kMaskDiag only
+  // the diagonal of the diagonal sub-tiles (a plain compare: the general
+  // form costs HEADMAX about 4 % even in the waves that skip it)
+  auto exclude = [&](lemo_f32x16& v, int a, int b) {
+    if (MASK == kMaskDiag) {
+      if (a == b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(lane, e) == l32) v[e] = 0.f;
+      }
+    } else {
+      mask_tile(v, a, b);
+    }
+  };
+
   lemo_f32x16 sum[2][2];          // PAPER: running sum over heads of max(0, S^h)
   lemo_f32x16 acc[2][2][2];       // [head parity][sub-tile]: S^h of the current and previous head
 #pragma unroll
@@ -263,7 +289,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
       for (int e = 0; e < 16; ++e)
         sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
     } else {
-      if (mask_wave) mask_tile(acc[P][a][b], a, b);
       int m = BLK >= 64 ? hm_lane : 0;
 #pragma unroll
       for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[P][a][b][e]));
@@ -326,9 +351,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            if (kc == 0 && s == 0)  // first k-step of a head: PAPER starts from the running sum, HEADMAX from 0
-              acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b],
-                                                                     MODE == 0 ? sum[a][b] : lemo_f32x16{}, 0, 0, 0);
+            if (kc == 0 && s == 0)  // first k-step of a head: the chain starts from 0
+              acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], lemo_f32x16{}, 0, 0, 0);
             else
               acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[P][a][b], 0, 0, 0);
           }
@@ -336,16 +360,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // HEADMAX: excluded pairs leave the head's tile before it is folded in
+    // (one pass, only in waves that hold such pairs, outside the
+    // interleaved fold so the common path keeps its schedule)
+    if (MODE == 1 && mask_wave) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) exclude(acc[P][a][b], a, b);
+    }
     if (MODE == 0) {
-      // acc = sum + S^h; sum >= 0 and a negative float is a negative integer,
-      // so sum = max(acc, sum) = sum + max(0, S^h) is one v_max_i32
+      // sum += max(0, S^h): a negative float is a negative integer, so the
+      // clamp is one v_max_i32 against 0
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            sum[a][b][e] = __int_as_float(imax(__float_as_int(acc[P][a][b][e]), __float_as_int(sum[a][b][e])));
+            sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
     }
   };
 
@@ -373,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) mask_tile(sum[a][b], a, b);
+        for (int b = 0; b < 2; ++b) exclude(sum[a][b], a, b);
     }
     if (BLK >= 64) {
       int m = 0;
@@ -469,22 +502,22 @@ __global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ M, int
   }
 }
 
-template <int HD, int MODE, bool CAUSAL>
+template <int HD, int MODE, int MASK>
 hipError_t launch_variant(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
                           long long bsq, long long bsk, int block, float scale, float* m, int nb, hipStream_t st) {
   const int ntq = (n + kTQ - 1) / kTQ, ntk = (n + kTK - 1) / kTK;
-  const dim3 grid(CAUSAL ? ntq * (ntq + 1) / 2 : ntq * ntk, n_batch), blk(kThreads);
+  const dim3 grid(MASK == kMaskCausal ? ntq * (ntq + 1) / 2 : ntq * ntk, n_batch), blk(kThreads);
   switch (block) {
     case 32:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 32, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 32, MASK>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
                          scale, m, nb, ntq, ntk);
       break;
     case 64:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 64, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 64, MASK>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
                          scale, m, nb, ntq, ntk);
       break;
     default:
-      hipLaunchKernelGGL((k_block_scores<HD, MODE, 128, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+      hipLaunchKernelGGL((k_block_scores<HD, MODE, 128, MASK>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
                          scale, m, nb, ntq, ntk);
       break;
   }
@@ -495,8 +528,11 @@ template <int HD, int MODE>
 hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
                           long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
                           hipStream_t st) {
-  return causal ? launch_variant<HD, MODE, true>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st)
-                : launch_variant<HD, MODE, false>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  if (causal)
+    return launch_variant<HD, MODE, kMaskCausal>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  if (n % block)
+    return launch_variant<HD, MODE, kMaskRagged>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  return launch_variant<HD, MODE, kMaskDiag>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
 }
 
 }  // namespace
