@@ -89,10 +89,19 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 
 __device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
 
+// Maximum over the wave's 64 lanes, as a wave-uniform value, without LDS
+// round trips: DPP swaps inside each row of 16 lanes (quad pairs, quad
+// halves, half-row mirror, row mirror) leave every lane of a row with the
+// row's maximum; the four row maxima are then read out as scalars.  (A
+// butterfly of __shfl_xor goes through LDS: six round trips per reduction;
+// the DPP form made HEADMAX, which reduces every head, 9% faster.)
 __device__ __forceinline__ int wave_imax(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = imax(v, __shfl_xor(v, off, 64));
-  return v;
+  v = imax(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = imax(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = imax(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = imax(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));   // row_mirror
+  return imax(imax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+              imax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 // Workgroup wg runs on XCD wg % 8 as its (wg / 8)-th workgroup there.  Give
@@ -476,6 +485,179 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   }
 }
 
+// One head (the per-token predictor's q_hat, k_hat of width r): PAPER and
+// HEADMAX coincide, M = max(0, block max of S), and a tile has only
+// HD / 64 chunks, so a workgroup walks `per_wg` consecutive logical tiles
+// with the loads of the next tile's first chunk in flight during the current
+// tile's last chunk (one pipeline over (tile, chunk)).  Same 128 x 128 tile,
+// waves, LDS ring, swizzle and exclusions as k_block_scores; the score tile
+// is reduced straight from the accumulators.  With blocks of 32 or 64 rows
+// each wave holds whole blocks and writes them itself, so there is no barrier
+// between tiles beyond the ring's.
+template <int HD, int BLK, int MASK>
+__global__ __launch_bounds__(kThreads, 2) void k_scores_one_head(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int ldq, int ldk, long long bsq,
+    long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk, int tiles_per_seq, int total,
+    int per_wg) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr int kCPH = HD / kChunk;
+  __shared__ float fin[kWaves];                          // 128-row blocks: per-wave maxima
+  const int rank = xcd_logical(blockIdx.x, gridDim.x);
+  const int t_begin = rank * per_wg, t_end = min(total, t_begin + per_wg);
+  if (t_begin >= t_end) return;                          // uniform: the whole workgroup leaves
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave >> 1, wk = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)g_stage;
+
+  // DMA: instruction i (Q: i < 4, K: i >= 4) of this wave fills row
+  // 32 ii + r0 of the tile's Q or K region; every such row has the same
+  // r & 15, so one swizzled piece offset serves all of them.
+  const int r0 = wave * 8 + (lane >> 3);
+  const uint32_t pc = (uint32_t)((((lane & 7) ^ swz(r0)) * 8) * 2);
+  struct Tile { int q0, k0; size_t qoff, koff, moff; bool mirror; };
+  auto tile = [&](int t) {
+    const int seq = t / tiles_per_seq;
+    int tq, tk;
+    if (CAUSAL)
+      tri_tile_of(t - seq * tiles_per_seq, ntq, tq, tk);
+    else
+      tile_of(t - seq * tiles_per_seq, ntq, ntk, tq, tk);
+    return Tile{tq * kTQ, tk * kTK, (size_t)seq * bsq, (size_t)seq * bsk, (size_t)seq * nb * nb, CAUSAL && tq != tk};
+  };
+  auto issue = [&](const Tile& tl, int kc, int stage) {
+    const uint16_t* qb = Q + tl.qoff + kc * kChunk;
+    const uint16_t* kb = K + tl.koff + kc * kChunk;
+    const uint32_t base = lds0 + (uint32_t)(stage * kStageBytes);
+#pragma unroll
+    for (int i = 0; i < kDmaPerChunk; ++i) {
+      const bool is_q = i < kDmaQ;
+      const int ii = is_q ? i : i - kDmaQ;
+      const int grow = min((is_q ? tl.q0 : tl.k0) + 32 * ii + r0, n_tokens - 1);   // rows past N: any valid row
+      const uint32_t voff = (uint32_t)((size_t)grow * (is_q ? ldq : ldk) * 2) + pc;
+      dma16(is_q ? (const void*)qb : (const void*)kb, voff,
+            base + (is_q ? 0u : (uint32_t)kStageQ) + (uint32_t)((ii * kWaves + wave) * 1024));
+    }
+  };
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int piece = (2 * s + hi) ^ swz(l32);
+    offA[s] = (uint32_t)((wq * 64 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
+  }
+  lemo_bf16x8 fa[2][2], fb[2][2];
+  auto read_frags = [&](int buf, const uint8_t* st, int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      fa[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + i * 32 * kRowBytes);
+      fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
+    }
+  };
+
+  Tile cur = tile(t_begin);
+  issue(cur, 0, 0);
+  int c = 0;                                             // chunks consumed so far: stage parity
+  for (int t = t_begin; t < t_end; ++t) {
+    Tile next = cur;
+    if (t + 1 < t_end) next = tile(t + 1);
+    lemo_f32x16 acc[2][2];
+#pragma unroll
+    for (int kc = 0; kc < kCPH; ++kc, ++c) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (kc + 1 < kCPH)
+        issue(cur, kc + 1, (c + 1) % kStages);
+      else if (t + 1 < t_end)
+        issue(next, 0, (c + 1) % kStages);
+      const uint8_t* st = g_stage + (c % kStages) * kStageBytes;
+      read_frags(0, st, 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int b0 = s & 1;
+        if (s + 1 < 4) read_frags(b0 ^ 1, st, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b0][a], fb[b0][b],
+                                                                (kc == 0 && s == 0) ? lemo_f32x16{} : acc[a][b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // exclusions (only in waves whose square holds such a pair), then the
+    // block maxima of max(0, S): an integer max from 0 on the float bits
+    const int qlo = cur.q0 + wq * 64, klo = cur.k0 + wk * 64;
+    const bool mask_wave = MASK == kMaskDiag
+                               ? klo == qlo
+                               : (CAUSAL ? klo >= qlo : klo == qlo) || qlo + 64 > n_tokens || klo + 64 > n_tokens;
+    if (mask_wave) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          int qb = qlo + a * 32 + 4 * hi;
+          int kr = klo + b * 32 + l32;
+          asm volatile("" : "+v"(qb), "+v"(kr));
+          const int dq = kr - qb;
+          const int lim = kr >= n_tokens ? 0 : n_tokens - qb;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 8 * (e >> 2) + (e & 3);
+            const bool out = MASK == kMaskDiag ? (a == b && r == dq)
+                                               : ((CAUSAL ? r <= dq : r == dq) || r >= lim);
+            if (out) acc[a][b][e] = 0.f;
+          }
+        }
+    }
+    float* Mt = M + cur.moff;
+    if (BLK == 32) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          int m = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+          m = wave_imax(m);
+          const int bq = (qlo + 32 * a) / 32, bk = (klo + 32 * b) / 32;
+          if (lane == 0 && bq < nb && bk < nb) {
+            Mt[(size_t)bq * nb + bk] = __int_as_float(m) * out_scale;
+            if (cur.mirror) Mt[(size_t)bk * nb + bq] = 0.f;
+          }
+        }
+    } else {
+      int m = 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+      m = wave_imax(m);
+      if (BLK == 64) {
+        const int bq = qlo / 64, bk = klo / 64;
+        if (lane == 0 && bq < nb && bk < nb) {
+          Mt[(size_t)bq * nb + bk] = __int_as_float(m) * out_scale;
+          if (cur.mirror) Mt[(size_t)bk * nb + bq] = 0.f;
+        }
+      } else {
+        // 128-row blocks: the four waves' maxima meet in LDS
+        if (lane == 0) fin[wave] = __int_as_float(m);
+        __syncthreads();
+        const int bq = cur.q0 / 128, bk = cur.k0 / 128;
+        if (tid == 0 && bq < nb && bk < nb) {
+          Mt[(size_t)bq * nb + bk] = fmaxf(fmaxf(fin[0], fin[1]), fmaxf(fin[2], fin[3])) * out_scale;
+          if (cur.mirror) Mt[(size_t)bk * nb + bq] = 0.f;
+        }
+      }
+    }
+    cur = next;
+  }
+}
+
 // Column sums I[c] = sum_r M[r][c].  A workgroup owns 16 columns; its 256
 // threads split the rows into 16 interleaved slices (thread (slice, column)
 // adds rows slice, slice+16, ... in order), then one thread per column adds
@@ -524,6 +706,43 @@ hipError_t launch_variant(const uint16_t* q, const uint16_t* k, int n_batch, int
   return hipGetLastError();
 }
 
+template <int HD, int MASK>
+hipError_t launch_one_head(const uint16_t* q, const uint16_t* k, int n_batch, int n, int ldq, int ldk, long long bsq,
+                           long long bsk, int block, float scale, float* m, int nb, hipStream_t st) {
+  const int ntq = (n + kTQ - 1) / kTQ, ntk = (n + kTK - 1) / kTK;
+  const int per_seq = MASK == kMaskCausal ? ntq * (ntq + 1) / 2 : ntq * ntk;
+  const int total = per_seq * n_batch;
+  // about 16 chunks per workgroup, but at least 1024 workgroups (4 per CU)
+  // while the tiles allow
+  const int want = (16 + HD / kChunk - 1) / (HD / kChunk);
+  const int per_wg = max(1, min(want, total / 1024));
+  const dim3 grid((total + per_wg - 1) / per_wg), blk(kThreads);
+  switch (block) {
+    case 32:
+      hipLaunchKernelGGL((k_scores_one_head<HD, 32, MASK>), grid, blk, 0, st, q, k, n, ldq, ldk, bsq, bsk, scale, m, nb,
+                         ntq, ntk, per_seq, total, per_wg);
+      break;
+    case 64:
+      hipLaunchKernelGGL((k_scores_one_head<HD, 64, MASK>), grid, blk, 0, st, q, k, n, ldq, ldk, bsq, bsk, scale, m, nb,
+                         ntq, ntk, per_seq, total, per_wg);
+      break;
+    default:
+      hipLaunchKernelGGL((k_scores_one_head<HD, 128, MASK>), grid, blk, 0, st, q, k, n, ldq, ldk, bsq, bsk, scale, m,
+                         nb, ntq, ntk, per_seq, total, per_wg);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_one_head_mask(const uint16_t* q, const uint16_t* k, int n_batch, int n, int ldq, int ldk,
+                                long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
+                                hipStream_t st) {
+  if (causal) return launch_one_head<HD, kMaskCausal>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  if (n % block) return launch_one_head<HD, kMaskRagged>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  return launch_one_head<HD, kMaskDiag>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+}
+
 template <int HD, int MODE>
 hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
                           long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
@@ -549,7 +768,12 @@ hipError_t lemo_launch_block_scores(const uint16_t* q, const uint16_t* k, int n_
   const double c = 1.0 / __builtin_sqrt((double)head_dim);
   const float scale = (float)(head_reduce == 0 ? c / n_heads : c);
   hipError_t e;
-  if (head_dim == 64)
+  if (n_heads == 1)   // both head reductions give max(0, block max of S)
+    e = head_dim == 64 ? launch_one_head_mask<64>(q, k, n_batch, n_tokens, ld_q, ld_k, bs_q, bs_k, block, causal,
+                                                  scale, m_out, nb, stream)
+                       : launch_one_head_mask<128>(q, k, n_batch, n_tokens, ld_q, ld_k, bs_q, bs_k, block, causal,
+                                                   scale, m_out, nb, stream);
+  else if (head_dim == 64)
     e = head_reduce == 0 ? launch_hd_mode<64, 0>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
                                                  causal, scale, m_out, nb, stream)
                          : launch_hd_mode<64, 1>(q, k, n_batch, n_tokens, n_heads, ld_q, ld_k, bs_q, bs_k, block,
