@@ -37,11 +37,10 @@ def kernel_source_hash() -> str:
 
 def _score_launches(trace_csv: str, timed_steps: int):
     """Per-dispatch durations (us) of the benchmark's exact-score launches,
-    in dispatch order, from the kernel-trace CSV.  The full-attention
-    instantiation also serves the per-token predictor's one-head scores
-    (a few percent of the 32-head time): only dispatches of at least half
-    the longest one count.  The bench times `timed_steps` steps right
-    before its first causal launch."""
+    in dispatch order, from the kernel-trace CSV.  Only dispatches of at
+    least half the longest one count (a much smaller launch of the same
+    instantiation would otherwise dilute the average).  The bench times
+    `timed_steps` steps right before its first causal launch."""
     rows = list(csv.DictReader(open(trace_csv)))
     seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
     full = [(s, (e - s) / 1e3) for s, e, n in seq if SCORE_KERNEL in n]
@@ -52,8 +51,8 @@ def _score_launches(trace_csv: str, timed_steps: int):
     many = [(s, d) for s, d in full if d >= 0.5 * top]
     first_causal = causal[0][0] if causal else None
     timed = [d for s, d in many if first_causal is None or s < first_causal][-timed_steps:]
-    lines = ["", f"{SCORE_KERNEL}, 32-head launches only ({len(full) - len(many)} one-head launches of the "
-             f"per-token predictor left out): {len(many)} launches, avg {sum(d for _, d in many) / len(many):.1f} us "
+    lines = ["", f"{SCORE_KERNEL}, 32-head launches only ({len(full) - len(many)} much smaller launches left "
+             f"out): {len(many)} launches, avg {sum(d for _, d in many) / len(many):.1f} us "
              "(includes the clock-settle launches)",
              f"  the {len(timed)} launches just before the first causal launch (the bench's timed steps): "
              f"avg {sum(timed) / max(len(timed), 1):.1f} us"]
@@ -98,9 +97,9 @@ def _per_kernel(counter_csv: str):
 
 
 def _many_heads(vals):
-    """The benchmark also runs the same instantiation with ONE head (the
-    per-token predictor's scores), which fetches a few percent of what the
-    32-head launch does: keep the dispatches within half of the largest."""
+    """Only the benchmark's 32-head launches: a launch of the same
+    instantiation on a much smaller problem would fetch a few percent of
+    theirs, so keep the dispatches within half of the largest."""
     top = max(vals)
     return [v for v in vals if v >= 0.5 * top]
 
@@ -110,8 +109,8 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, command
     w_score, w_causal, w_copy = _per_kernel(write_csv)
     if not (f_all and w_score and f_copy and w_copy):
         raise SystemExit("missing score-kernel or copy-probe dispatches in the counter files")
-    # fetch: the 32-head launches only; write (M, 256 KiB, the same for one
-    # head or 32) is averaged over every launch of the instantiation
+    # fetch: the 32-head launches only; write (M, 256 KiB) is averaged over
+    # every launch of the instantiation
     f_score = _many_heads(f_all)
     # the copy probe is the copyBuffer dispatch with the largest reading
     # (uploads of the inputs are host-to-device and smaller)
@@ -151,8 +150,8 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, command
                 f"WRITE_SIZE avg {sum(w_score) / len(w_score):.0f} KiB\n")
         f.write(f"  -> HBM bytes per launch: read {fetch_b / 1e9:.3f} GB, write {write_b / 1e9:.4f} GB, "
                 f"total {(fetch_b + write_b) / 1e9:.3f} GB\n")
-        f.write(f"  ({len(f_all) - len(f_score)} one-head launches of the same instantiation, the per-token "
-                f"predictor's scores, left out of the fetch average)\n")
+        f.write(f"  ({len(f_all) - len(f_score)} much smaller launches of the same instantiation left out of the "
+                f"fetch average)\n")
         if causal:
             f.write(f"{CAUSAL_KERNEL}: {causal['launches']} launches -> HBM bytes per launch: read "
                     f"{causal['fetch_bytes_per_launch'] / 1e9:.3f} GB, write "
