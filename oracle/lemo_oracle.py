@@ -184,18 +184,23 @@ def pool_blocks(x, block: int) -> np.ndarray:
     a representative embedding from each block"; the pages do not define it).
 
     Reading: the mean of the block's rows.  The sum is taken in float32, row by
-    row in token order, times 1/block (exact for the power-of-two block sizes
-    accepted), then rounded to bf16, because the result feeds a bf16 product.
-    Returns bf16 bits [nb][d]."""
+    row in token order, divided by the number of rows in float32 (for a whole
+    block of a power-of-two size that is the exact multiplication by 1/block),
+    then rounded to bf16, because the result feeds a bf16 product.  When N is
+    not a multiple of the block size the last block holds the N mod b
+    remaining rows and is averaged over those.  Returns bf16 bits [nb][d]."""
     if block & (block - 1):
         raise ValueError("block must be a power of two")
     X = bf16_decode(x).astype(np.float32)
     n_tok, d = X.shape
-    X3 = X.reshape(n_tok // block, block, d)
-    acc = np.zeros((n_tok // block, d), dtype=np.float32)
-    for i in range(block):
-        acc = acc + X3[:, i, :]                  # float32 add, rows in order
-    mean = acc * np.float32(1.0 / block)
+    nb = -(-n_tok // block)
+    mean = np.empty((nb, d), dtype=np.float32)
+    for m in range(nb):
+        rows = X[m * block:min((m + 1) * block, n_tok)]
+        acc = np.zeros(d, dtype=np.float32)
+        for row in rows:
+            acc = acc + row                      # float32 add, rows in order
+        mean[m] = acc / np.float32(len(rows))
     return bf16_round(mean.astype(np.float64))
 
 
@@ -283,10 +288,22 @@ def select_mask(scores, mode: int, threshold: float = 0.0, keep_blocks: int = 0)
 # --------------------------------------------------------------------------
 # a6 / a7: permutation-free movement
 # --------------------------------------------------------------------------
-def kept_token_rows(kept, n_kept: int, block: int) -> np.ndarray:
-    """Original row of every kept token, in kept-block order."""
+def kept_token_rows(kept, n_kept: int, block: int, n_tokens: int = None) -> np.ndarray:
+    """Original row of every kept token, in kept-block order: packed row
+    p = j * block + i is token kept[j] * block + i.  With n_tokens given and
+    not a multiple of the block size, the last block has only the remaining
+    rows: the packed rows end after the last kept block's rows (an ascending
+    kept list, as select_mask gives, holds that short block last), and a
+    position whose token lies past the sequence (the short block listed
+    before the end) is -1: no row is read or written for it."""
     kept = np.asarray(kept[:n_kept], dtype=np.int64)
-    return (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    rows = (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    if n_tokens is None or n_kept == 0:
+        return rows
+    R = (n_kept - 1) * block + min(block, n_tokens - int(kept[-1]) * block)
+    rows = rows[:R].copy()
+    rows[rows >= n_tokens] = -1
+    return rows
 
 
 def gather_pad(src, block: int, kept, n_kept: int, dst_init, pad_multiple: int):
@@ -298,12 +315,13 @@ def gather_pad(src, block: int, kept, n_kept: int, dst_init, pad_multiple: int):
     Returns (dst bits, overflowed)."""
     dst = np.array(dst_init, dtype=np.uint16, copy=True)
     cap = dst.shape[0]
-    rows = kept_token_rows(kept, n_kept, block)
+    rows = kept_token_rows(kept, n_kept, block, np.asarray(src).shape[0])
     n_rows = rows.size
     n_pad = -(-n_rows // pad_multiple) * pad_multiple
     width = min(dst.shape[1], np.asarray(src).shape[1])
     for p in range(min(n_rows, cap)):
-        dst[p, :width] = src[rows[p], :width]
+        if rows[p] >= 0:
+            dst[p, :width] = src[rows[p], :width]
     for p in range(n_rows, min(n_pad, cap)):
         dst[p, :width] = 0
     return dst, n_pad > cap
@@ -326,13 +344,14 @@ def gather_linear(x, block: int, kept, n_kept: int, weight, dst_init, pad_multip
     dropped and reported.  Returns (dst bits, overflowed)."""
     dst = np.array(dst_init, dtype=np.uint16, copy=True)
     cap = dst.shape[0]
-    rows = kept_token_rows(kept, n_kept, block)
+    rows = kept_token_rows(kept, n_kept, block, np.asarray(x).shape[0])
     n_rows = rows.size
     n_pad = -(-n_rows // pad_multiple) * pad_multiple
     take = min(n_rows, cap)
     width = np.asarray(weight).shape[0]
-    if take:
-        dst[:take, :width] = linear_bf16(np.asarray(x)[rows[:take]], weight)
+    live = np.nonzero(rows[:take] >= 0)[0]
+    if live.size:
+        dst[live, :width] = linear_bf16(np.asarray(x)[rows[live]], weight)
     for p in range(n_rows, min(n_pad, cap)):
         dst[p, :width] = 0
     return dst, n_pad > cap
@@ -343,7 +362,7 @@ def linear_scatter(a, weight, residual, block: int, kept, n_kept: int):
     Figure 18).  Reading: row p of a (the dense kept rows) times weightᵀ,
     rounded to bf16, then added to the original row of kept token p exactly as
     `scatter_residual` adds it.  Returns new residual bits."""
-    rows = kept_token_rows(kept, n_kept, block)
+    rows = kept_token_rows(kept, n_kept, block, np.asarray(residual).shape[0])
     y = linear_bf16(np.asarray(a)[:rows.size], weight) if rows.size else np.zeros((0, 0), np.uint16)
     return scatter_residual(residual, block, kept, n_kept, y)
 
@@ -356,11 +375,12 @@ def scatter_residual(residual, block: int, kept, n_kept: int, y):
     formed in float64, where two bf16 values add exactly unless one is
     negligible, then rounded once).  Returns new residual bits."""
     out = np.array(residual, dtype=np.uint16, copy=True)
-    rows = kept_token_rows(kept, n_kept, block)
+    rows = kept_token_rows(kept, n_kept, block, out.shape[0])
     width = out.shape[1]
     y = np.asarray(y)
     for p, t in enumerate(rows):
-        out[t] = bf16_round(bf16_decode(out[t]) + bf16_decode(y[p, :width]))
+        if t >= 0:
+            out[t] = bf16_round(bf16_decode(out[t]) + bf16_decode(y[p, :width]))
     return out
 
 
@@ -376,11 +396,12 @@ def residual_recompute(residual_out, block: int, kept, n_kept: int, y):
     spacing at the output value plus half a spacing at the result.
     Returns new residual bits."""
     out = np.array(residual_out, dtype=np.uint16, copy=True)
-    rows = kept_token_rows(kept, n_kept, block)
+    rows = kept_token_rows(kept, n_kept, block, out.shape[0])
     width = out.shape[1]
     y = np.asarray(y)
     for p, t in enumerate(rows):
-        out[t] = bf16_round(bf16_decode(out[t]) - bf16_decode(y[p, :width]))
+        if t >= 0:
+            out[t] = bf16_round(bf16_decode(out[t]) - bf16_decode(y[p, :width]))
     return out
 
 

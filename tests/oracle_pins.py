@@ -693,6 +693,43 @@ def check_recompute(o) -> list:
     return out
 
 
+def check_ragged_tail(o) -> list:
+    """A last block shorter than the others: hand example E11 (its mean,
+    gather with padding, in-place addition, and the position map when the
+    short block is listed before the end); a block of identical rows pools to
+    that row whatever its length; whole blocks are unchanged by a ragged
+    tail."""
+    out = []
+    e = golden()["E11_ragged_tail"]
+    b = e["block"]
+    x = f2bits(np.array(e["x"]))
+    _fail(out, np.array_equal(o.bf16_decode(o.pool_blocks(x, b)), np.array(e["xbar"])), "E11 pooled means")
+    kept = np.array(e["kept"], np.int32)
+    dst, over = o.gather_pad(x, b, kept, 2, np.full((6, 2), 0x7777, np.uint16), e["gather_pad_multiple"])
+    _fail(out, np.array_equal(o.bf16_decode(dst[:4]), np.array(e["gathered"])) and np.all(dst[4:] == 0x7777)
+          and not over, f"E11 gather {dst.tolist()}")
+    res = o.scatter_residual(x, b, kept, 2, f2bits(np.array(e["y"])))
+    _fail(out, np.array_equal(o.bf16_decode(res), np.array(e["residual_after"])), f"E11 scatter {o.bf16_decode(res)}")
+    back = o.residual_recompute(res, b, kept, 2, f2bits(np.array(e["y"])))
+    _fail(out, np.array_equal(back, x), "E11 recompute of exact additions")
+    rows = o.kept_token_rows(np.array(e["kept_misplaced"], np.int32), 2, b, 5)
+    _fail(out, rows.tolist() == e["rows_misplaced"], f"E11 misplaced short block rows {rows.tolist()}")
+    dstm, _ = o.gather_pad(x, b, np.array(e["kept_misplaced"], np.int32), 2, np.full((4, 2), 0x7777, np.uint16), 1)
+    _fail(out, np.all(dstm[1] == 0x7777) and np.array_equal(dstm[0], x[4]) and np.array_equal(dstm[2:], x[:2]),
+          "E11 misplaced short block: position 1 must be left untouched")
+    # identical rows in every block, the short one included, pool to the row
+    rng = np.random.default_rng(17)
+    for n, blk in ((7, 4), (13, 8), (9, 2)):
+        base = torch_bf16_bits(rng.standard_normal((-(-n // blk), 6)).astype(np.float32))
+        xs = np.repeat(base, blk, axis=0)[:n]
+        _fail(out, np.array_equal(o.pool_blocks(xs, blk), base), f"identical rows do not pool to the row (n={n} b={blk})")
+    # whole blocks do not see the ragged tail
+    xr = torch_bf16_bits(rng.standard_normal((21, 8)).astype(np.float32))
+    _fail(out, np.array_equal(o.pool_blocks(xr, 4)[:5], o.pool_blocks(xr[:20], 4)), "ragged tail changes whole blocks")
+    return out
+
+
 ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
               check_exact_closed_form, check_exact_invariants, check_predictor, check_token_predictor,
-              check_select, check_movement, check_fused_movement, check_mlp_scores, check_recompute]
+              check_select, check_movement, check_fused_movement, check_mlp_scores, check_recompute,
+              check_ragged_tail]

@@ -34,7 +34,16 @@ MUTATIONS = [
      [P.check_exact_hand]),
     ("causal_reversed", "(j_abs[None, :] >= i_abs[:, None]) if causal", "(j_abs[None, :] <= i_abs[:, None]) if causal",
      [P.check_exact_hand]),
-    ("tail_block_dropped", "nb = -(-n_tok // block)", "nb = n_tok // block", [P.check_exact_hand]),
+    ("tail_block_dropped", "nb = -(-n_tok // block)\n    Q = bf16_decode(q)", "nb = n_tok // block\n    Q = bf16_decode(q)",
+     [P.check_exact_hand]),
+    ("pool_tail_divides_by_block", "mean[m] = acc / np.float32(len(rows))", "mean[m] = acc / np.float32(block)",
+     [P.check_ragged_tail]),
+    ("pool_tail_dropped", "nb = -(-n_tok // block)\n    mean = np.empty", "nb = n_tok // block\n    mean = np.empty",
+     [P.check_ragged_tail]),
+    ("kept_rows_tail_full", "R = (n_kept - 1) * block + min(block, n_tokens - int(kept[-1]) * block)",
+     "R = n_kept * block", [P.check_ragged_tail]),
+    ("kept_rows_misplaced_not_skipped", "rows[rows >= n_tokens] = -1", "rows[rows >= n_tokens] = 0",
+     [P.check_ragged_tail]),
     ("tail_block_full_width", "rows_of = [np.arange(m * block, min((m + 1) * block, n_tok)) for m in kb]",
      "rows_of = [np.arange(m * block, (m + 1) * block) % n_tok for m in kb]", [P.check_exact_bruteforce]),
     ("empty_block_pair_not_zero", "M[a] = np.maximum(best, 0.0)", "M[a] = best", [P.check_exact_hand]),
@@ -47,7 +56,7 @@ MUTATIONS = [
     ("max_before_clamp_swapped", "M[a] = np.maximum(per_head, 0.0).sum(axis=0)", "M[a] = np.maximum(per_head.sum(axis=0), 0.0)",
      [P.check_exact_closed_form]),
     ("predictor_no_clamp", "M = np.maximum(q_hat @ k_hat.T, 0.0)", "M = q_hat @ k_hat.T", [P.check_predictor]),
-    ("pool_sum_not_mean", "mean = acc * np.float32(1.0 / block)", "mean = acc", [P.check_predictor]),
+    ("pool_sum_not_mean", "mean[m] = acc / np.float32(len(rows))", "mean[m] = acc", [P.check_predictor]),
     ("predictor_no_relu", "hid = np.maximum(bf16_decode(xbar) @ bf16_decode(u), 0.0)",
      "hid = bf16_decode(xbar) @ bf16_decode(u)", [P.check_predictor]),
     ("predictor_transposed_v", "return bf16_decode(hid_bf16) @ bf16_decode(v)",
@@ -58,8 +67,8 @@ MUTATIONS = [
      [P.check_token_predictor]),
     ("linear_weight_not_transposed", "prod = bf16_decode(a) @ bf16_decode(weight).T", "prod = bf16_decode(a) @ bf16_decode(weight)",
      [P.check_fused_movement]),
-    ("gather_linear_dense_rows", "dst[:take, :width] = linear_bf16(np.asarray(x)[rows[:take]], weight)",
-     "dst[:take, :width] = linear_bf16(np.asarray(x)[:take], weight)", [P.check_fused_movement]),
+    ("gather_linear_dense_rows", "dst[live, :width] = linear_bf16(np.asarray(x)[rows[live]], weight)",
+     "dst[live, :width] = linear_bf16(np.asarray(x)[live], weight)", [P.check_fused_movement]),
     ("gather_linear_no_pad", "        dst[p, :width] = 0\n    return dst, n_pad > cap\n\n\ndef linear_scatter",
      "        pass\n    return dst, n_pad > cap\n\n\ndef linear_scatter", [P.check_fused_movement]),
     ("threshold_strict", "keep = s >= theta\n    elif mode == SELECT_MEAN", "keep = s > theta\n    elif mode == SELECT_MEAN",
@@ -71,16 +80,16 @@ MUTATIONS = [
     ("round_ties_away", "r = np.rint(np.ldexp(ax, -qexp))", "r = np.floor(np.ldexp(ax, -qexp) + 0.5)",
      [P.check_bf16_round]),
     ("round_no_subnormals", "qexp = np.maximum(e - 8, -133)", "qexp = e - 8", [P.check_bf16_round]),
-    ("gather_wrong_block", "return (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)",
-     "return ((kept[:, None] + 1) * block + np.arange(block)[None, :]).reshape(-1) % 6", [P.check_movement]),
+    ("gather_wrong_block", "rows = (kept[:, None] * block + np.arange(block)[None, :]).reshape(-1)",
+     "rows = ((kept[:, None] + 1) * block + np.arange(block)[None, :]).reshape(-1) % 6", [P.check_movement]),
     ("pad_not_zeroed", "        dst[p, :width] = 0\n    return dst, n_pad > cap\n\n\ndef linear_bf16",
      "        pass\n    return dst, n_pad > cap\n\n\ndef linear_bf16", [P.check_movement]),
-    ("scatter_into_dense_rows", "for p, t in enumerate(rows):\n        out[t] = bf16_round(bf16_decode(out[t]) +",
-     "for p, t in enumerate(range(rows.size)):\n        out[t] = bf16_round(bf16_decode(out[t]) +", [P.check_movement]),
+    ("scatter_into_dense_rows", "for p, t in enumerate(rows):\n        if t >= 0:\n            out[t] = bf16_round(bf16_decode(out[t]) +",
+     "for p, t in enumerate(range(rows.size)):\n        if t >= 0:\n            out[t] = bf16_round(bf16_decode(out[t]) +", [P.check_movement]),
     ("recompute_adds", "bf16_decode(out[t]) - bf16_decode(y[p, :width])", "bf16_decode(out[t]) + bf16_decode(y[p, :width])",
      [P.check_recompute]),
-    ("recompute_into_dense_rows", "for p, t in enumerate(rows):\n        out[t] = bf16_round(bf16_decode(out[t]) -",
-     "for p, t in enumerate(range(rows.size)):\n        out[t] = bf16_round(bf16_decode(out[t]) -", [P.check_recompute]),
+    ("recompute_into_dense_rows", "for p, t in enumerate(rows):\n        if t >= 0:\n            out[t] = bf16_round(bf16_decode(out[t]) -",
+     "for p, t in enumerate(range(rows.size)):\n        if t >= 0:\n            out[t] = bf16_round(bf16_decode(out[t]) -", [P.check_recompute]),
     ("recompute_y_misaligned", "bf16_decode(out[t]) - bf16_decode(y[p, :width])", "bf16_decode(out[t]) - bf16_decode(y[t, :width])",
      [P.check_recompute]),
     ("mlp_no_magnitude", "_block_channel_max_sum(np.abs(bf16_decode(act)), block)", "_block_channel_max_sum(bf16_decode(act), block)",
