@@ -163,7 +163,7 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
 }
 
 size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int rank) {
-  if (n_tokens <= 0 || block <= 0 || n_tokens % block || d_model <= 0 || rank <= 0) return 0;
+  if (n_tokens <= 0 || block <= 0 || d_model <= 0 || rank <= 0) return 0;
   return lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
 }
 
@@ -174,7 +174,6 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
   REQUIRE(scores != nullptr && u_q && v_q && u_k && v_k, LEMO_ERR_INVALID_ARG, "scores or a predictor matrix is NULL");
   REQUIRE(n_tokens > 0 && block > 0 && d_model > 0 && rank > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d d_model=%d rank=%d)", n_tokens, block, d_model, rank);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(pow2(block) && block >= 2 && block <= 256, LEMO_ERR_UNSUPPORTED, "block %d (power of two, 2..256)", block);
   REQUIRE(d_model % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_model %d (multiple of 64 supported)", d_model);
   REQUIRE(rank % 32 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 32, at most 256)", rank);
@@ -242,7 +241,6 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
   REQUIRE(n_tokens > 0 && block > 0 && width > 0 && cap_rows > 0 && pad_multiple > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d width=%d cap_rows=%d pad_multiple=%d)", n_tokens, block,
           width, cap_rows, pad_multiple);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   lemo_status st;
   if ((st = check_rows(src, ld_src, width, "src")) != LEMO_OK) return st;
@@ -258,7 +256,6 @@ lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, 
   REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
   REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   lemo_status st;
   if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
@@ -274,7 +271,6 @@ lemo_status lemo_residual_recompute(lemo_bf16* residual, int n_tokens, int width
   REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
   REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   lemo_status st;
   if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
@@ -332,7 +328,6 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
   REQUIRE(n_tokens > 0 && block > 0 && d_in > 0 && d_out > 0 && cap_rows > 0 && pad_multiple > 0,
           LEMO_ERR_INVALID_ARG, "sizes must be positive (n_tokens=%d block=%d d_in=%d d_out=%d cap_rows=%d pad=%d)",
           n_tokens, block, d_in, d_out, cap_rows, pad_multiple);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
   lemo_status st;
@@ -353,7 +348,6 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
   REQUIRE(n_tokens > 0 && block > 0 && d_in > 0 && d_out > 0 && cap_rows > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d d_in=%d d_out=%d cap_rows=%d)", n_tokens, block, d_in, d_out,
           cap_rows);
-  REQUIRE(n_tokens % block == 0, LEMO_ERR_INVALID_ARG, "n_tokens %d is not a multiple of block %d", n_tokens, block);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
   lemo_status st;

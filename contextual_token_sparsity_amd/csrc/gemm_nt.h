@@ -27,7 +27,9 @@
 //   kEpiScatterAdd A rows dense; the product is added in place to residual
 //                  row tok(m): res = bf16(f32(res) + f32(bf16(acc))), m < R
 // with tok(m) = kept[m / block] * block + m % block and R = n_kept * block
-// read on the device.  Rows whose kept index is out of range are skipped and
+// read on the device (less the rows the short last block of a ragged
+// sequence lacks, when it is the last kept block).  Rows whose kept index is
+// out of range, or whose token lies past the sequence, are skipped and
 // flagged, as the stand-alone gather and scatter do.
 #pragma once
 
@@ -117,10 +119,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   // rows in use: all M, or the kept rows (plus zero padding for the gather)
   int R = M, rows_used = M, nb = 0;
   if (kMapped) {
-    nb = rm.n_tokens / rm.block;
+    nb = (rm.n_tokens + rm.block - 1) / rm.block;
     const int nk = *rm.n_kept;
     const bool bad = nk < 0 || nk > nb;
     R = bad ? 0 : nk * rm.block;
+    if (!bad && nk > 0) {
+      // the short last block of a ragged sequence, when it is the last kept
+      // block, has fewer rows
+      const int last = rm.kept[nk - 1];
+      if (last >= 0 && last < nb) R -= max(0, (last + 1) * rm.block - rm.n_tokens);
+    }
     if (EPI == kEpiGather) {
       const long long pad = ((long long)R + rm.pad_multiple - 1) / rm.pad_multiple * rm.pad_multiple;
       rows_used = (int)min((long long)M, pad);
@@ -144,10 +152,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   }
   if (m0 >= rows_used) return;   // the whole workgroup: before any barrier
 
-  // token row of kept row m, or -1 (index out of range)
+  // token row of kept row m, or -1 (index out of range, or a row past the
+  // sequence: the short last block listed before the end)
   auto tok_of = [&](int m) {
     const int blk = rm.kept[m / rm.block];
-    return (blk >= 0 && blk < nb) ? blk * rm.block + m % rm.block : -1;
+    const int t = blk * rm.block + m % rm.block;
+    return (blk >= 0 && blk < nb && t < rm.n_tokens) ? t : -1;
   };
 
   const int tid = threadIdx.x, lane = tid & 63;

@@ -52,10 +52,22 @@ __device__ __forceinline__ uint4 add_bf16x8(uint4 a, uint4 b) {
   return o;
 }
 
-// Original token row of dense row p, or -1 when its kept index is invalid.
-__device__ __forceinline__ int token_of(const int32_t* __restrict__ kept, int p, int block, int nb) {
+// Original token row of dense row p, or -1 when its kept index is invalid or
+// the row lies past the sequence (the short last block of a ragged sequence
+// listed before the end of the kept list).
+__device__ __forceinline__ int token_of(const int32_t* __restrict__ kept, int p, int block, int nb, int n_tokens) {
   const int blk = kept[p / block];
-  return (blk >= 0 && blk < nb) ? blk * block + p % block : -1;
+  const int t = blk * block + p % block;
+  return (blk >= 0 && blk < nb && t < n_tokens) ? t : -1;
+}
+
+// Dense rows of the kept blocks: n_kept whole blocks, less the rows the short
+// last block of a ragged sequence lacks when it is the last kept block.
+__device__ __forceinline__ int kept_rows(const int32_t* __restrict__ kept, int nk, int block, int nb, int n_tokens) {
+  if (nk <= 0) return 0;
+  const int last = kept[nk - 1];
+  const int short_by = (last >= 0 && last < nb) ? max(0, (last + 1) * block - n_tokens) : 0;
+  return nk * block - short_by;
 }
 
 __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict__ src, int n_tokens, int width,
@@ -63,10 +75,10 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ n_kept_p, uint16_t* __restrict__ dst,
                                                      int ld_dst, int cap_rows, int pad_multiple,
                                                      int32_t* __restrict__ status) {
-  const int nb = n_tokens / block;
+  const int nb = (n_tokens + block - 1) / block;
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
-  const int n_rows = bad_count ? 0 : nk * block;
+  const int n_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
   const long long n_pad = ((long long)n_rows + pad_multiple - 1) / pad_multiple * pad_multiple;
   const int rows = (int)min((long long)cap_rows, n_pad);
   if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
@@ -87,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
       v[u] = make_uint4(0, 0, 0, 0);
       tok[u] = -1;
       if (p < n_rows) {
-        tok[u] = token_of(kept, p, block, nb);
+        tok[u] = token_of(kept, p, block, nb, n_tokens);
         if (tok[u] >= 0) v[u] = load_stream(src + (size_t)tok[u] * ld_src + ch * 8);
       }
     }
@@ -111,10 +123,10 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
                                                       const int32_t* __restrict__ n_kept_p,
                                                       const uint16_t* __restrict__ y, int ld_y,
                                                       int32_t* __restrict__ status) {
-  const int nb = n_tokens / block;
+  const int nb = (n_tokens + block - 1) / block;
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
-  const int n_rows = bad_count ? 0 : nk * block;
+  const int n_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
   if (status && bad_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
     atomicOr(status, LEMO_DEV_BAD_KEPT);
   const int ch = blockIdx.x * kThreads + threadIdx.x;
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
 #pragma unroll
     for (int u = 0; u < kUnrollScatter; ++u) {
       const int p = p0 + u * step;
-      tok[u] = p < n_rows ? token_of(kept, p, block, nb) : -2;
+      tok[u] = p < n_rows ? token_of(kept, p, block, nb, n_tokens) : -2;
       if (tok[u] >= 0) {
         r[u] = load_stream(res + (size_t)tok[u] * ld_res + ch * 8);
         a[u] = load_stream(y + (size_t)p * ld_y + ch * 8);

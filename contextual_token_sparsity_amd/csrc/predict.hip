@@ -5,7 +5,8 @@
 // is aggregated along the column like the exact scores.
 //
 // Pipeline (all on the caller's stream, workspace carved by the host):
-//   k_pool        xbar[m] = bf16((sum of the block's rows, fp32, in row order) / block)
+//   k_pool        xbar[m] = bf16((sum of the block's rows, fp32, in row order) / its row
+//                 count: block, or fewer for the last block of a ragged sequence)
 //                 -- one pass over X, the only HBM-heavy phase.
 //   k_hidden      part[s][m][n] = xbar[m, Ks] . [U_q | U_k][Ks, n]  (bf16 MFMA,
 //                 split over s = slices Ks of d_model so that ~1000 waves run)
@@ -22,16 +23,18 @@ namespace {
 // in order, so every column sum is formed in the same order as a sequential
 // loop.  64 threads cover 512 columns; the grid is (column groups, blocks).
 __global__ __launch_bounds__(64) void k_pool(const uint16_t* __restrict__ X, int ld, int d, int block,
-                                             float inv_block, uint16_t* __restrict__ xbar) {
+                                             int n_tokens, float inv_block, uint16_t* __restrict__ xbar) {
   const int m = blockIdx.y;
   const int c8 = blockIdx.x * 64 + threadIdx.x;
   if (c8 * 8 >= d) return;
   const uint16_t* p = X + (size_t)m * block * ld + c8 * 8;
+  // the last block of a ragged sequence holds only the remaining rows
+  const int rows = min(block, n_tokens - m * block);
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 #pragma unroll 8
-  for (int i = 0; i < block; ++i) {
+  for (int i = 0; i < rows; ++i) {
     const uint4 v = *reinterpret_cast<const uint4*>(p + (size_t)i * ld);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -40,11 +43,19 @@ __global__ __launch_bounds__(64) void k_pool(const uint16_t* __restrict__ X, int
       acc[2 * j + 1] += lemo_bf16_to_f32(w[j] >> 16);
     }
   }
+  // a whole block: times 1/block, exact for its power-of-two size; a short
+  // one: an IEEE division by its row count
+  if (rows == block) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv_block;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = acc[j] / (float)rows;
+  }
   uint4 o;
   uint32_t* ow = &o.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    ow[j] = lemo_f32_to_bf16(acc[2 * j] * inv_block) | (lemo_f32_to_bf16(acc[2 * j + 1] * inv_block) << 16);
+  for (int j = 0; j < 4; ++j) ow[j] = lemo_f32_to_bf16(acc[2 * j]) | (lemo_f32_to_bf16(acc[2 * j + 1]) << 16);
   *reinterpret_cast<uint4*>(xbar + (size_t)m * d + c8 * 8) = o;
 }
 
@@ -152,7 +163,7 @@ struct Layout {
 };
 
 Layout layout(int n_tokens, int d_model, int block, int rank) {
-  const int nb = n_tokens / block;
+  const int nb = (n_tokens + block - 1) / block;
   const int s = lemo_predict_splitk(nb, d_model, rank);
   Layout L;
   size_t off = 0;
@@ -184,7 +195,7 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
                                const uint16_t* u_q, const uint16_t* v_q, const uint16_t* u_k,
                                const uint16_t* v_k, int rank, float* m_out, float* scores, void* workspace,
                                hipStream_t st) {
-  const int nb = n_tokens / block;
+  const int nb = (n_tokens + block - 1) / block;
   const Layout L = layout(n_tokens, d_model, block, rank);
   char* ws = static_cast<char*>(workspace);
   uint16_t* xbar = reinterpret_cast<uint16_t*>(ws + L.xbar);
@@ -193,7 +204,7 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
   float* khat = reinterpret_cast<float*>(ws + L.khat);
   float* M = m_out ? m_out : reinterpret_cast<float*>(ws + L.m);
 
-  hipLaunchKernelGGL(k_pool, dim3((d_model / 8 + 63) / 64, nb), dim3(64), 0, st, x, ld_x, d_model, block,
+  hipLaunchKernelGGL(k_pool, dim3((d_model / 8 + 63) / 64, nb), dim3(64), 0, st, x, ld_x, d_model, block, n_tokens,
                      1.0f / (float)block, xbar);
   const int s = lemo_predict_splitk(nb, d_model, rank);
   const int n_mt = (nb + 31) / 32, n_nt = (2 * rank) / 32;

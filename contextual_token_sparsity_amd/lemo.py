@@ -175,7 +175,7 @@ def lemo_predict_scores(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, 
     n = x.shape[0]
     d = x.shape[1] if d_model is None else d_model
     rank = u_q.shape[1]
-    nb = n // block
+    nb = -(-n // block)                 # a ragged last block counts
     if scores is None:
         scores = torch.empty(nb, dtype=torch.float32, device=x.device)
     if workspace is None:

@@ -161,14 +161,17 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
  * Predicted block scores (Jenga 4.2.2, Eq. 3 and Figure 8).
  *
  * Each token block's representative embedding is the mean of its rows,
- *   xbar_m = bf16( (fp32 sum of the block's rows, in row order) / block );
+ *   xbar_m = bf16( (fp32 sum of the block's rows, in row order) / rows );
+ * rows = block, or for the last block of a ragged sequence (n_tokens not a
+ * multiple of block) the n_tokens mod block remaining rows (an IEEE fp32
+ * division; for a whole block it is the exact multiplication by 1/block);
  * the query and key predictors are q_hat = bf16(ReLU(xbar U_q)) V_q and
  * k_hat = bf16(ReLU(xbar U_k)) V_k (fp32 accumulation; q_hat, k_hat fp32);
  * the block-pair score is M_hat[m][n] = max(0, q_hat_m . k_hat_n) and the
  * token block score is the column aggregate I_hat[n] = sum over m of M_hat[m][n].
  *
  *  x             bf16 [n_tokens][ld_x] token embeddings, d_model columns used.
- *  block         power of two, 2..256; n_tokens a multiple of it.
+ *  block         power of two, 2..256; nb = ceil(n_tokens / block).
  *  d_model       multiple of 64.   rank: multiple of 32, at most 256.
  *  u_q, u_k      bf16 [d_model][rank] row-major.  v_q, v_k: bf16 [rank][rank].
  *  block_scores  optional fp32 [nb][nb] M_hat (NULL: kept in workspace).
@@ -239,6 +242,13 @@ lemo_status lemo_select_mask(const float* scores, int n_blocks, int mode, float 
  *  pad_multiple)-1 are zeroed; rows beyond are not touched.  Rows at or past
  *  cap_rows are never written (LEMO_DEV_CAP_OVERFLOW is set if R rounded up
  *  exceeds cap_rows).  n_kept and kept_blocks are read on the device.
+ *  Ragged sequences (n_tokens not a multiple of block): the last block
+ *  (index nb - 1) has only n_tokens mod block rows; when it is the last kept
+ *  block, as in lemo_select_mask's ascending list, R is that many rows short
+ *  of n_kept * block.  A position whose token would lie past n_tokens (the
+ *  short block listed before the end) is skipped and flags
+ *  LEMO_DEV_BAD_KEPT, like an out-of-range kept index.  The same holds for
+ *  lemo_scatter_residual, lemo_residual_recompute and the fused products.
  *  width         multiple of 8; ld_src, ld_dst >= width, multiples of 8.
  *  cap_rows      rows of dst.   pad_multiple >= 1.
  * ------------------------------------------------------------------------ */
@@ -285,8 +295,10 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
  * added to that token's original row of the residual stream; eliminated
  * tokens are left bit-identical.
  *
- *  residual[t] = bf16_rne(fp32(residual[t]) + fp32(y[p])) for p < n_kept*block,
- *  t = kept_blocks[p / block] * block + p % block, over `width` elements.
+ *  residual[t] = bf16_rne(fp32(residual[t]) + fp32(y[p])) for p < R,
+ *  t = kept_blocks[p / block] * block + p % block, over `width` elements
+ *  (R as for lemo_gather_pad: n_kept*block, less the missing rows of a
+ *  ragged sequence's short last block).
  *  (fp32 add then round-to-nearest-even: the correctly rounded bf16 sum.)
  *  y             bf16 [>= n_kept*block][ld_y], rows in kept order (as
  *                lemo_gather_pad lays them out).

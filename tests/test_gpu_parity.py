@@ -296,6 +296,108 @@ def test_causal_full_size_sampled():
         assert not Mg[np.triu_indices(nb, 1)].any()
 
 
+# ------------------------------- ragged last block: predictor and movement calls
+PRED_RAGGED = [
+    # (N, d, block, rank): the last block holds N mod block rows
+    (1000, 256, 64, 64),
+    (200, 128, 32, 32),
+    (130, 512, 64, 128),
+    (4000, 192, 256, 96),
+]
+
+
+@pytest.mark.parametrize("shape", PRED_RAGGED, ids=lambda s: "N%d_d%d_b%d_r%d" % s)
+def test_predict_ragged(shape):
+    n, d, b, r = shape
+    say("predict ragged", shape)
+    x, w = _pred_inputs(n + d + r + 1, n, d, r)
+    nb = -(-n // b)
+    M_ref, I_ref, _, _ = O.predict_scores(x, *w, b)
+    assert M_ref.shape == (nb, nb)
+    M = torch.full((nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_predict_scores(dev(x), *[dev(a) for a in w], b, block_scores=M)
+    Ig, Mg = I.cpu().numpy(), M.cpu().numpy()
+    ok, worst = scores_close(Ig, I_ref)
+    assert ok and worst < 1e-3, worst
+    merr = np.abs(Mg - M_ref) <= 1e-2 * np.abs(M_ref) + 1e-3 * np.abs(M_ref).max()
+    assert merr.all(), float(np.abs(Mg - M_ref).max())
+
+
+MOVE_RAGGED = [
+    # (N, width, block, kept blocks, pad_multiple): kept lists as select gives them
+    # (ascending), with and without the short last block, and one that lists the
+    # short block first (its missing rows are skipped and flagged)
+    (1000, 256, 64, [1, 4, 5, 9, 15], 64),          # short last block (40 rows) kept
+    (1000, 256, 64, [0, 3, 8, 14], 64),             # short block dropped
+    (200, 64, 32, list(range(7)), 1),               # keep all: 6 x 32 + 8 rows = N
+    (1000, 128, 64, [15, 2, 9], 32),                # short block listed first
+]
+
+
+@pytest.mark.parametrize("case", MOVE_RAGGED,
+                         ids=lambda c: "N%d_w%d_b%d_%s" % (c[0], c[1], c[2], "-".join(map(str, c[3]))))
+def test_movement_ragged(case):
+    n, w, b, kept_l, pad = case
+    say("movement ragged", case)
+    rng = np.random.default_rng(n + w + len(kept_l))
+    nb = -(-n // b)
+    kept = np.array(kept_l, np.int32)
+    nk = kept.size
+    misplaced = nk and kept[:-1].max(initial=-1) == nb - 1 and n % b
+    rows = O.kept_token_rows(kept, nk, b, n)
+    R = rows.size
+    cap = -(-R // pad) * pad + 3
+    src = synth.random_bf16(rng, (n, w))
+    kept_d = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    kept_d[:nk] = torch.from_numpy(kept).cuda()
+    nk_d = torch.tensor([nk], dtype=torch.int32, device="cuda")
+    expect_status = lemo.DEV_BAD_KEPT if misplaced else 0
+    # gather with padding
+    sentinel = np.full((cap, w), 0x5A5A, np.uint16)
+    dst_ref, over = O.gather_pad(src, b, kept, nk, sentinel, pad)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dstd = dev(sentinel)
+    lemo.lemo_gather_pad(dev(src), b, kept_d, nk_d, dstd, pad_multiple=pad, dev_status=status)
+    assert np.array_equal(host_bits(dstd), dst_ref) and not over
+    assert int(status.item()) == expect_status
+    # in-place addition, then its backward recompute
+    res = synth.random_bf16(rng, (n, w))
+    y = synth.random_bf16(rng, (max(R, 1), w), 0.1)
+    ref = O.scatter_residual(res, b, kept, nk, y)
+    resd = dev(res)
+    status.zero_()
+    lemo.lemo_scatter_residual(resd, b, kept_d, nk_d, dev(y), dev_status=status)
+    assert np.array_equal(host_bits(resd), ref)
+    assert int(status.item()) == expect_status
+    back_ref = O.residual_recompute(ref, b, kept, nk, y)
+    lemo.lemo_residual_recompute(resd, b, kept_d, nk_d, dev(y))
+    assert np.array_equal(host_bits(resd), back_ref)
+    # the same movement fused into products (d_in = width, a multiple of 64)
+    wt = synth.random_bf16(rng, (72, w), 1.0 / math.sqrt(w))
+    ysent = np.full((cap, 72), 0x5A5A, np.uint16)
+    yref, _ = O.gather_linear(src, b, kept, nk, wt, ysent, pad)
+    yd = dev(ysent)
+    status.zero_()
+    lemo.lemo_gather_linear(dev(src), b, kept_d, nk_d, dev(wt), yd, pad_multiple=pad, dev_status=status)
+    got = host_bits(yd)
+    live = rows >= 0
+    ok, same = _embeddings_close(got[:R][live], yref[:R][live])
+    assert ok, same
+    assert np.array_equal(got[:R][~live], yref[:R][~live]) and np.array_equal(got[R:], yref[R:])
+    assert int(status.item()) == expect_status
+    a = synth.random_bf16(rng, (max(R, 1), w))
+    w2 = synth.random_bf16(rng, (w, w), 1.0 / math.sqrt(w))
+    sref = O.linear_scatter(a, w2, res, b, kept, nk)
+    r2 = dev(res)
+    lemo.lemo_linear_scatter(dev(a), dev(w2), r2, b, kept_d, nk_d)
+    got2 = host_bits(r2)
+    touched = np.zeros(n, bool)
+    touched[rows[rows >= 0]] = True
+    assert np.array_equal(got2[~touched], res[~touched])
+    ok, same = _embeddings_close(got2[touched], sref[touched])
+    assert ok, same
+
+
 # ------------------------------------------------------------- predictor
 PRED_SMALL = [
     # (N, d, block, rank)
