@@ -286,35 +286,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   float total[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // HEADMAX, blocks <= 64 rows: sum over heads
   int hm_lane = 0;                                // HEADMAX, blocks >= 64: this lane's running block max
 
-  // Folds sub-tile t = (a, b) of a finished head (accumulators acc[P]) into
-  // the cross-head state.  Runs interleaved with the next head's MFMAs.
+  // HEADMAX: folds sub-tile t = (a, b) of a finished head (accumulators
+  // acc[P]) into the cross-head state (the clamped block maxima summed over
+  // heads).  Runs interleaved with the next head's MFMAs.
   auto finalize = [&](auto P_, int t, int h) {
     constexpr int P = decltype(P_)::value;
     const int a = t >> 1, b = t & 1;
-    if (MODE == 0) {
-      // sum += max(0, S): the bit pattern of a negative float is a negative
-      // integer, so v_max_i32 against 0 is the ReLU
+    int m = BLK >= 64 ? hm_lane : 0;
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
-    } else {
-      int m = BLK >= 64 ? hm_lane : 0;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[P][a][b][e]));
-      if (BLK >= 64) {
-        hm_lane = m;
-        if (t == 3) {  // all four sub-tiles lie in one block: reduce across lanes
-          m = wave_imax(m);
-          hm_lane = 0;
-          if (BLK == 128) {
-            if (lane == 0) part[wave][h] = __int_as_float(m);
-          } else {
-            total[0][0] += __int_as_float(m);
-          }
+    for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[P][a][b][e]));
+    if (BLK >= 64) {
+      hm_lane = m;
+      if (t == 3) {  // all four sub-tiles lie in one block: reduce across lanes
+        m = wave_imax(m);
+        hm_lane = 0;
+        if (BLK == 128) {
+          if (lane == 0) part[wave][h] = __int_as_float(m);
+        } else {
+          total[0][0] += __int_as_float(m);
         }
-      } else {
-        total[a][b] += __int_as_float(wave_imax(m));
       }
+    } else {
+      total[a][b] += __int_as_float(wave_imax(m));
     }
   };
 
