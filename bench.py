@@ -67,8 +67,8 @@ def load_traffic(causal=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU sharding "
-              "is described in DESIGN.md and not measured", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); sharding the path over "
+              "several GPUs is a design note, not a measured configuration", file=sys.stderr)
         sys.exit(2)
     import torch
     from contextual_token_sparsity_amd import lemo, synth
