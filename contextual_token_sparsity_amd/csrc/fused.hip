@@ -23,8 +23,8 @@ hipError_t lemo_launch_gather_linear(const uint16_t* x, int n_tokens, int d_in, 
   const dim3 grid = grid_for(128, cap_rows, d_out, 1, tm, tn);
   const Args g = {{x, x}, {w, w}, {y, y}};
   const RowMap rm = {kept, n_kept, block, n_tokens, pad_multiple, dev_status};
-  hipLaunchKernelGGL((k_gemm_nt<kEpiGather, 128>), grid, dim3(kThreads), 0, st, g, ld_x, ld_w, cap_rows, d_out, d_in, ld_y,
-                     tm, tn, rm);
+  hipLaunchKernelGGL((k_gemm_nt<kEpiGather, 128>), grid, dim3(kThreads), 0, st, g, ld_x, ld_w, cap_rows, d_out, d_in,
+                     ld_y, tm, tn, rm);
   return hipGetLastError();
 }
 
