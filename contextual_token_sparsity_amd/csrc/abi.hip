@@ -42,6 +42,15 @@ lemo_status check_rows(const void* p, int ld, int width, const char* name) {
   return LEMO_OK;
 }
 
+// The matrix-core kernels load rows straight into LDS with a 32-bit per-lane
+// byte offset from the matrix base (the column offset goes into the 64-bit
+// base), so rows x ld must stay below 2^31 elements.
+lemo_status check_offsets(int rows, int ld, const char* name) {
+  REQUIRE((long long)(rows > 0 ? rows - 1 : 0) * ld < (1LL << 31) - 64, LEMO_ERR_UNSUPPORTED,
+          "%s: %d rows x ld %d is beyond 32-bit row offsets", name, rows, ld);
+  return LEMO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +101,8 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
   lemo_status st;
   if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
   if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_q, "q")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_k, "k")) != LEMO_OK) return st;
   float* m_out = block_scores;
   if (!m_out) {
     const size_t need = lemo_block_scores_workspace(n_tokens, block);
@@ -138,6 +149,8 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
   lemo_status st;
   if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
   if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_q, "q")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_k, "k")) != LEMO_OK) return st;
   if (n_batch > 1) {
     // each sequence's rows are 16-byte aligned, and sequences do not overlap
     REQUIRE(batch_stride_q % 8 == 0 && batch_stride_k % 8 == 0, LEMO_ERR_ALIGNMENT,
@@ -206,6 +219,8 @@ lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model,
   REQUIRE(rank % 64 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 64, at most 256)", rank);
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, 2 * rank, "hidden layer")) != LEMO_OK) return st;
   if ((st = check_rows(q_hat, ld_out, rank, "q_hat")) != LEMO_OK) return st;
   if ((st = check_rows(k_hat, ld_out, rank, "k_hat")) != LEMO_OK) return st;
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
@@ -334,6 +349,8 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
   if ((st = check_rows(x, ld_x, d_in, "x")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
   if ((st = check_rows(y, ld_y, d_out, "y")) != LEMO_OK) return st;
+  if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
+  if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
   return device_status(lemo_launch_gather_linear(x, n_tokens, d_in, ld_x, block, kept_blocks, n_kept, weight, d_out,
                                                  ld_w, y, ld_y, cap_rows, pad_multiple, dev_status,
                                                  static_cast<hipStream_t>(stream)),
@@ -354,6 +371,8 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
   if ((st = check_rows(a, ld_a, d_in, "a")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
   if ((st = check_rows(residual, ld_res, d_out, "residual")) != LEMO_OK) return st;
+  if ((st = check_offsets(cap_rows, ld_a, "a")) != LEMO_OK) return st;
+  if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
   return device_status(lemo_launch_linear_scatter(a, d_in, ld_a, cap_rows, weight, d_out, ld_w, residual, n_tokens,
                                                   ld_res, block, kept_blocks, n_kept, dev_status,
                                                   static_cast<hipStream_t>(stream)),

@@ -38,7 +38,11 @@
  *    int32 `dev_status` word (the caller clears it): LEMO_DEV_CAP_OVERFLOW,
  *    LEMO_DEV_NONFINITE, LEMO_DEV_BAD_KEPT.
  *  - Pointers to bf16 matrices must be 16-byte aligned and their ld a
- *    multiple of 8 elements (128-bit row access).
+ *    multiple of 8 elements (128-bit row access).  Matrices read by the
+ *    matrix-core kernels (q, k, x of the per-token predictor and of the
+ *    fused products, a, weight) are addressed with 32-bit row offsets:
+ *    (rows - 1) * ld must stay below 2^31 - 64 elements, else the call
+ *    returns LEMO_ERR_UNSUPPORTED.
  *  - Inputs and outputs of one call must not overlap, except the residual of
  *    lemo_scatter_residual, lemo_residual_recompute and lemo_linear_scatter,
  *    which is updated in place by design.

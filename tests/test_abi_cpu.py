@@ -262,3 +262,20 @@ def test_ragged_sequences_pass_validation(L):
     assert L.lemo_scatter_residual(P, 1000, 64, 64, 64, P, P, NULL, 64, NULL, NULL) == INVALID      # y NULL
     assert L.lemo_residual_recompute(P, 1000, 64, 64, 64, P, P, NULL, 64, NULL, NULL) == INVALID    # y NULL
     assert "multiple of block" not in lemo.lemo_last_error()
+
+
+def test_row_offsets_must_fit_32_bits(L):
+    """The matrix-core kernels address rows with 32-bit byte offsets: rows x ld
+    must stay below 2^31 elements, else the call is refused (never wraps)."""
+    # exact scores: 2^21 tokens with rows of 4096 elements is 2^33 elements
+    assert bs(L, n=1 << 21, h=32, hd=128, ldq=4096, ldk=4096) == UNSUP
+    assert "32-bit" in lemo.lemo_last_error()
+    assert bsb(L, B=1, n=1 << 21, h=32, hd=128, ldq=4096, ldk=4096) == UNSUP
+    # per-token predictor embeddings: wide x
+    assert te(L, n=1 << 20, d=4096, ldx=4096) == UNSUP
+    # fused products: token rows of x, and the weight
+    big = 1 << 20
+    assert L.lemo_gather_linear(P, big, 4096, 4096, 64, P, P, P, 64, 4096, P, 64, 256, 1, NULL, NULL) == UNSUP
+    assert L.lemo_linear_scatter(P, 64, 64, 16, P, 1 << 22, 1024, P, 1024, 1 << 22, 64, P, P, NULL, NULL) == UNSUP
+    # just below the limit passes these checks (and stops at the missing workspace)
+    assert bs(L, n=(1 << 19), h=32, hd=128, ldq=4096, ldk=4096, M=NULL, ws=NULL) == WS
