@@ -71,9 +71,12 @@ const char* lemo_last_error(void) { return g_last_error.c_str(); }
 
 int lemo_version(void) { return 100; }  // 0.1.0
 
-// Exact scores: the tile grid (at most (N/128)^2 workgroups) stays within a
-// launch's 2^31 workgroups and the block matrix within 2^40 entries.
+// Exact scores: the block matrix stays within 2^40 entries.  A launch's x
+// dimension holds at most 2^31 - 1 work-items, i.e. 2^23 workgroups of 256:
+// with more than one head every 128 x 128 tile is a workgroup, so a launch
+// takes at most 2^23 tiles (one head: the workgroups walk ranges of tiles).
 constexpr int kMaxScoreTokens = 1 << 22;
+constexpr long long kMaxWorkgroups = 1LL << 23;
 
 size_t lemo_block_scores_workspace(int n_tokens, int block) {
   if (n_tokens <= 0 || block <= 0 || n_tokens % block) return 0;
@@ -98,6 +101,9 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
           block);
   REQUIRE(head_reduce == LEMO_REDUCE_PAPER || n_heads <= 128, LEMO_ERR_UNSUPPORTED,
           "HEADMAX supports at most 128 heads (got %d)", n_heads);
+  const long long ntq = (n_tokens + 127) / 128;
+  REQUIRE(n_heads == 1 || ntq * ntq <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "%lld tiles in one launch (at most %lld with more than one head)", ntq * ntq, kMaxWorkgroups);
   lemo_status st;
   if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
   if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
@@ -144,8 +150,9 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
   const int nb = (n_tokens + block - 1) / block;
   const long long ntq = (n_tokens + 127) / 128;
   const long long tiles = (flags & LEMO_SCORES_CAUSAL) ? ntq * (ntq + 1) / 2 : ntq * ntq;
-  REQUIRE(n_batch * tiles <= 0x7fffffffLL, LEMO_ERR_UNSUPPORTED,
-          "n_batch * tiles = %lld exceeds one launch (n_batch=%d n_tokens=%d)", n_batch * tiles, n_batch, n_tokens);
+  REQUIRE(n_batch * tiles <= (n_heads == 1 ? 0x7fffffffLL : kMaxWorkgroups), LEMO_ERR_UNSUPPORTED,
+          "n_batch * tiles = %lld exceeds one launch (n_batch=%d n_tokens=%d n_heads=%d)", n_batch * tiles, n_batch,
+          n_tokens, n_heads);
   lemo_status st;
   if ((st = check_rows(q, ld_q, n_heads * head_dim, "q")) != LEMO_OK) return st;
   if ((st = check_rows(k, ld_k, n_heads * head_dim, "k")) != LEMO_OK) return st;
@@ -190,6 +197,8 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
   REQUIRE(pow2(block) && block >= 2 && block <= 256, LEMO_ERR_UNSUPPORTED, "block %d (power of two, 2..256)", block);
   REQUIRE(d_model % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_model %d (multiple of 64 supported)", d_model);
   REQUIRE(rank % 32 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 32, at most 256)", rank);
+  REQUIRE((n_tokens + block - 1) / block <= 65535, LEMO_ERR_UNSUPPORTED, "%d blocks (at most 65535)",
+          (n_tokens + block - 1) / block);
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
@@ -221,6 +230,8 @@ lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model,
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, 2 * rank, "hidden layer")) != LEMO_OK) return st;
+  REQUIRE((n_tokens + 63) / 64 * (long long)((2 * rank + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "n_tokens %d: too many tiles for one launch", n_tokens);
   if ((st = check_rows(q_hat, ld_out, rank, "q_hat")) != LEMO_OK) return st;
   if ((st = check_rows(k_hat, ld_out, rank, "k_hat")) != LEMO_OK) return st;
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
@@ -309,6 +320,8 @@ static lemo_status mlp_scores(const char* fn, const lemo_bf16* act, int ld_act, 
           "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   REQUIRE(lemo_mlp_chunks(width) <= 65535, LEMO_ERR_UNSUPPORTED, "width %d too large", width);
+  REQUIRE((n_tokens + block - 1) / block <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED, "%d blocks (at most %lld)",
+          (n_tokens + block - 1) / block, kMaxWorkgroups);
   lemo_status st;
   if ((st = check_rows(act, ld_act, width, up ? "gate" : "act")) != LEMO_OK) return st;
   if (up && (st = check_rows(up, ld_up, width, "up")) != LEMO_OK) return st;
@@ -351,6 +364,8 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
   if ((st = check_rows(y, ld_y, d_out, "y")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
+  REQUIRE((cap_rows + 127LL) / 128 * ((d_out + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "cap_rows %d x d_out %d: too many tiles for one launch", cap_rows, d_out);
   return device_status(lemo_launch_gather_linear(x, n_tokens, d_in, ld_x, block, kept_blocks, n_kept, weight, d_out,
                                                  ld_w, y, ld_y, cap_rows, pad_multiple, dev_status,
                                                  static_cast<hipStream_t>(stream)),
@@ -373,6 +388,8 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
   if ((st = check_rows(residual, ld_res, d_out, "residual")) != LEMO_OK) return st;
   if ((st = check_offsets(cap_rows, ld_a, "a")) != LEMO_OK) return st;
   if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
+  REQUIRE((cap_rows + 127LL) / 128 * ((d_out + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "cap_rows %d x d_out %d: too many tiles for one launch", cap_rows, d_out);
   return device_status(lemo_launch_linear_scatter(a, d_in, ld_a, cap_rows, weight, d_out, ld_w, residual, n_tokens,
                                                   ld_res, block, kept_blocks, n_kept, dev_status,
                                                   static_cast<hipStream_t>(stream)),

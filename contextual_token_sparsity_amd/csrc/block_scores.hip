@@ -708,7 +708,8 @@ hipError_t launch_one_head(const uint16_t* q, const uint16_t* k, int n_batch, in
   // about 16 chunks per workgroup, but at least 1024 workgroups (4 per CU)
   // while the tiles allow
   const int want = (16 + HD / kChunk - 1) / (HD / kChunk);
-  const int per_wg = max(1, min(want, total / 1024));
+  // and at most 2^23 workgroups (a launch's x dimension holds 2^31 - 1 work-items)
+  const int per_wg = max(max(1, min(want, total / 1024)), (int)((total + (1LL << 23) - 1) >> 23));
   const dim3 grid((total + per_wg - 1) / per_wg), blk(kThreads);
   switch (block) {
     case 32:

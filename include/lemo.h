@@ -104,7 +104,9 @@ typedef enum {
  *
  *  q, k          bf16 [n_tokens][ld_q|ld_k]; head h occupies columns
  *                h*head_dim .. h*head_dim+head_dim-1.
- *  n_tokens      N > 0, a multiple of block, at most 2^22.
+ *  n_tokens      N > 0, a multiple of block, at most 2^22; with more than
+ *                one head at most 2^23 tiles of 128 x 128 per launch
+ *                (N <= 370688).
  *  head_dim      64 or 128.   block: 32, 64 or 128.
  *  block_scores  optional fp32 [nb][nb] output M (row n = query block),
  *                nb = n_tokens / block; NULL keeps M in the workspace.
@@ -150,7 +152,8 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
  * Errors: as lemo_block_scores, plus INVALID_ARG (n_batch < 1, unknown
  * flags, stride smaller than a sequence), UNSUPPORTED (n_batch > 65535, or
  * n_batch times the 128 x 128 tiles of one sequence -- ceil(N/128)^2, or
- * T(ceil(N/128)) = t (t + 1) / 2 with the causal flag -- above 2^31 - 1),
+ * T(ceil(N/128)) = t (t + 1) / 2 with the causal flag -- above 2^23 with
+ * more than one head, above 2^31 - 1 with one),
  * ALIGNMENT (stride not a multiple of 8).
  * ------------------------------------------------------------------------ */
 #define LEMO_SCORES_CAUSAL 1
@@ -175,7 +178,7 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
  * token block score is the column aggregate I_hat[n] = sum over m of M_hat[m][n].
  *
  *  x             bf16 [n_tokens][ld_x] token embeddings, d_model columns used.
- *  block         power of two, 2..256; nb = ceil(n_tokens / block).
+ *  block         power of two, 2..256; nb = ceil(n_tokens / block) <= 65535.
  *  d_model       multiple of 64.   rank: multiple of 32, at most 256.
  *  u_q, u_k      bf16 [d_model][rank] row-major.  v_q, v_k: bf16 [rank][rank].
  *  block_scores  optional fp32 [nb][nb] M_hat (NULL: kept in workspace).

@@ -267,10 +267,11 @@ def test_ragged_sequences_pass_validation(L):
 def test_row_offsets_must_fit_32_bits(L):
     """The matrix-core kernels address rows with 32-bit byte offsets: rows x ld
     must stay below 2^31 elements, else the call is refused (never wraps)."""
-    # exact scores: 2^21 tokens with rows of 4096 elements is 2^33 elements
-    assert bs(L, n=1 << 21, h=32, hd=128, ldq=4096, ldk=4096) == UNSUP
+    # exact scores (one head: no tile limit): 2^21 tokens in rows of 4096 elements is 2^33 elements
+    assert bs(L, n=1 << 21, h=1, hd=128, ldq=4096, ldk=4096) == UNSUP
     assert "32-bit" in lemo.lemo_last_error()
-    assert bsb(L, B=1, n=1 << 21, h=32, hd=128, ldq=4096, ldk=4096) == UNSUP
+    assert bsb(L, B=1, n=1 << 21, h=1, hd=128, ldq=4096, ldk=4096) == UNSUP
+    assert "32-bit" in lemo.lemo_last_error()
     # per-token predictor embeddings: wide x
     assert te(L, n=1 << 20, d=4096, ldx=4096) == UNSUP
     # fused products: token rows of x, and the weight
@@ -278,4 +279,19 @@ def test_row_offsets_must_fit_32_bits(L):
     assert L.lemo_gather_linear(P, big, 4096, 4096, 64, P, P, P, 64, 4096, P, 64, 256, 1, NULL, NULL) == UNSUP
     assert L.lemo_linear_scatter(P, 64, 64, 16, P, 1 << 22, 1024, P, 1024, 1 << 22, 64, P, P, NULL, NULL) == UNSUP
     # just below the limit passes these checks (and stops at the missing workspace)
-    assert bs(L, n=(1 << 19), h=32, hd=128, ldq=4096, ldk=4096, M=NULL, ws=NULL) == WS
+    assert bs(L, n=(1 << 19), h=1, hd=128, ldq=4096, ldk=4096, M=NULL, ws=NULL) == WS
+
+
+def test_launch_grid_limits(L):
+    """A launch holds at most 2^23 workgroups in x: more than one head takes at
+    most 2^23 tiles of 128 x 128 (one head walks ranges of tiles, so any size
+    up to 2^22 tokens passes); the predictor's pooling takes at most 65535
+    blocks."""
+    assert bs(L, n=1 << 22, h=2, hd=64, ldq=128, ldk=128) == UNSUP
+    assert "tiles" in lemo.lemo_last_error()
+    assert bs(L, n=2896 * 128, h=2, hd=64, ldq=128, ldk=128, M=NULL, ws=NULL) == WS
+    assert bs(L, n=1 << 22, h=1, hd=64, ldq=64, ldk=64, M=NULL, ws=NULL) == WS
+    assert bsb(L, B=2, n=2896 * 128, h=2, hd=64, ldq=128, ldk=128, sq=2896 * 128 * 128, sk=2896 * 128 * 128,
+               flags=0) == UNSUP
+    assert ps(L, n=65536 * 2 + 2, b=2, ws=NULL) == UNSUP
+    assert ps(L, n=65535 * 2, b=2, ws=NULL) == WS

@@ -134,6 +134,36 @@ def test_exact_closed_form_full_size(mode):
     assert ok, worst
 
 
+@pytest.mark.parametrize("h,n", [(2, 2896 * 128), (1, 1 << 22)], ids=["two_heads", "one_head"])
+def test_exact_max_tokens_closed_form(h, n):
+    """The largest accepted sequences against the rank-one closed form
+    I[m] = nb a max_{j in m} beta_j / sqrt(hd): with two heads 370688 tokens
+    (2896^2 tiles, just under the 2^23 workgroups of one launch), with one
+    head 2^22 tokens (a 32768 x 32768 block matrix of 4 GiB, the one-head
+    kernel's workgroups walking ranges of 2^30 tiles).  Rows of h x 64
+    elements, blocks of 128; checks every column score and sampled block
+    pairs, one of them past 2^31 entries of M when N = 2^22."""
+    hd, b = 64, 128
+    nb = n // b
+    say("exact max tokens", h)
+    rng = np.random.default_rng(23)
+    a = 0.5
+    beta = synth.to_bf16_bits((np.abs(rng.standard_normal(n)) + 0.01).astype(np.float32))
+    bf = synth.bf16_bits_to_f32(beta).astype(np.float64)
+    q = np.zeros((n, h * hd), np.uint16)
+    k = np.zeros((n, h * hd), np.uint16)
+    q[:, 7::hd] = synth.to_bf16_bits(np.full((1,), a, np.float32))[0]
+    k[:, 7::hd] = beta[:, None]
+    M = torch.empty((nb, nb), device="cuda")
+    I, _ = lemo.lemo_block_scores(dev(q), dev(k), h, hd, b, O.REDUCE_PAPER, block_scores=M)
+    col = a * bf.reshape(nb, b).max(axis=1) / math.sqrt(hd)
+    ok, worst = scores_close(I.cpu().numpy(), nb * col, rel=1e-5)
+    assert ok, worst
+    for (r, c) in ((nb - 1, nb - 1), (nb - 1, 5), (nb * 5 // 8, nb * 7 // 8)):
+        assert abs(float(M[r, c]) - col[c]) <= 1e-5 * col[c], (r, c, float(M[r, c]), col[c])
+    del M
+
+
 def test_exact_deterministic():
     q, k = rand_qk(77, 1024, 4, 128)
     outs = []
