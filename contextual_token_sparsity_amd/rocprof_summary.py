@@ -8,7 +8,11 @@
     # (rocprofv3 --pmc FETCH_SIZE / --pmc WRITE_SIZE of `bench.py --copy-probe`)
     python -m contextual_token_sparsity_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_TXT "COMMANDS"
 
-The counters are calibrated on the plain 1 GiB device-to-device copy that
+    # where the exact-score kernel's cycles go, from two counter runs of
+    # `bench.py` (SQ/GRBM/TCP counters listed in BUSY_PASSES)
+    python -m contextual_token_sparsity_amd.rocprof_summary busy PASS1_CSV PASS2_CSV OUT_TXT "COMMANDS"
+
+The traffic counters are calibrated on the plain 1 GiB device-to-device copy that
 `bench.py --copy-probe` issues: the ratio of its known bytes to what each
 counter reports scales the exact-score kernel's readings.
 """
@@ -159,12 +163,99 @@ def traffic(fetch_csv: str, write_csv: str, out_json: str, out_txt: str, command
         f.write(f"kernel source sha256[:16]: {kernel_source_hash()}\n")
 
 
+# counter passes for `busy` (each within one run's per-block limits: at most
+# 8 SQ counters; GRBM_GUI_ACTIVE in both, since it times each dispatch)
+BUSY_PASSES = (
+    "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVE_CYCLES "
+    "SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CU_CYCLES",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VMEM SQ_INSTS_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_LDS_BANK_CONFLICT "
+    "TCP_PENDING_STALL_CYCLES_sum",
+)
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def _dispatch_counters(counter_csv: str):
+    """{dispatch id: (duration s, {counter: value})} of the exact-score
+    kernel's 32-head launches."""
+    per = defaultdict(dict)
+    dur = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if SCORE_KERNEL not in r["Kernel_Name"]:
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] = float(r["Counter_Value"])
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not per:
+        raise SystemExit(f"no {SCORE_KERNEL} dispatches in {counter_csv}")
+    top = max(v.get("GRBM_GUI_ACTIVE", 0.0) for v in per.values())
+    return {d: (dur[d], v) for d, v in per.items() if v.get("GRBM_GUI_ACTIVE", 0.0) >= 0.5 * top}
+
+
+def busy(pass1_csv: str, pass2_csv: str, out_txt: str, commands: str) -> None:
+    """Cycle-level figures of the exact-score kernel.  GRBM_GUI_ACTIVE is
+    summed over the 8 XCDs, so a launch takes GRBM/8 shader cycles and
+    GRBM/8/duration is the clock it ran at; SQ_VALU_MFMA_BUSY_CYCLES is
+    summed over the 1024 SIMDs."""
+    p1, p2 = _dispatch_counters(pass1_csv), _dispatch_counters(pass2_csv)
+
+    def avg(p, name):
+        vals = [v[name] for _, v in p.values() if name in v]
+        return sum(vals) / len(vals) if vals else float("nan")
+
+    cyc1 = avg(p1, "GRBM_GUI_ACTIVE") / N_XCD
+    cyc2 = avg(p2, "GRBM_GUI_ACTIVE") / N_XCD
+    # the clock of the last launches of the first pass (the earliest run
+    # while the clock is still rising)
+    last = sorted(p1)[-10:]
+    clocks = [p1[d][1]["GRBM_GUI_ACTIVE"] / N_XCD / p1[d][0] for d in last]
+    clock = sum(clocks) / len(clocks)
+    mfma_busy = avg(p1, "SQ_VALU_MFMA_BUSY_CYCLES") / N_SIMD
+    n_mfma = avg(p1, "SQ_INSTS_MFMA")
+    lds_active = avg(p1, "SQ_LDS_IDX_ACTIVE") / N_CU
+    n_lds = avg(p1, "SQ_INSTS_LDS")
+    wave_cyc = avg(p1, "SQ_WAVE_CYCLES") * 4           # the SQ wave counters tick every 4 cycles
+    wait_any = avg(p1, "SQ_WAIT_ANY") * 4
+    wait_inst = avg(p1, "SQ_WAIT_INST_ANY") * 4
+    n_vmem = avg(p2, "SQ_INSTS_VMEM")
+    n_valu = avg(p2, "SQ_INSTS_VALU")
+    coexec = avg(p2, "SQ_VALU_MFMA_COEXEC_CYCLES") / N_SIMD
+    conflicts = avg(p2, "SQ_LDS_BANK_CONFLICT")
+    tcp_pending = avg(p2, "TCP_PENDING_STALL_CYCLES_sum") / N_CU
+    lines = [
+        "# where the exact-score kernel's cycles go (rocprofv3 counters)",
+        f"# commands: {commands}",
+        "",
+        f"{SCORE_KERNEL}: {len(p1)} + {len(p2)} launches (32-head launches of the two passes)",
+        f"cycles per launch (GRBM_GUI_ACTIVE / 8 XCDs): {cyc1:.4g} (pass 1), {cyc2:.4g} (pass 2)",
+        f"clock under this load (cycles / launch duration, last {len(last)} launches of pass 1): "
+        f"{clock / 1e9:.2f} GHz",
+        f"MFMA instructions per launch: {n_mfma:.4g}; busy cycles per SIMD: {mfma_busy:.4g} "
+        f"({mfma_busy / cyc1:.1%} of the launch's cycles)",
+        f"  -> at {clock / 1e9:.2f} GHz that is {mfma_busy / cyc1 * clock / 2.4e9:.1%} of the dense bf16 peak "
+        "quoted at 2.4 GHz",
+        f"LDS: {n_lds:.4g} instructions, index-active {lds_active:.4g} cycles per CU "
+        f"({lds_active / cyc1:.1%} of the cycles), {lds_active * N_CU / max(n_lds, 1):.2f} cycles per instruction, "
+        f"bank conflicts {conflicts:.4g}",
+        f"waves: {wave_cyc:.4g} wave-cycles, waiting on anything {wait_any / wave_cyc:.1%}, "
+        f"waiting to issue {wait_inst / wave_cyc:.1%}",
+        f"VMEM (direct-to-LDS refills): {n_vmem:.4g} instructions; vector L1 stalled on pending L2 data "
+        f"{tcp_pending:.4g} cycles per CU ({tcp_pending / cyc2:.1%})",
+        f"VALU: {n_valu:.4g} instructions (MFMA included); MFMA busy while a VALU op issued: "
+        f"{coexec:.4g} cycles per SIMD",
+        f"kernel source sha256[:16]: {kernel_source_hash()}",
+    ]
+    with open(out_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1] if len(sys.argv) > 1 else ""
     if cmd == "trace" and len(sys.argv) in (5, 6):
         trace(*sys.argv[2:])
     elif cmd == "traffic" and len(sys.argv) == 7:
         traffic(*sys.argv[2:7])
+    elif cmd == "busy" and len(sys.argv) == 6:
+        busy(*sys.argv[2:6])
     else:
         print(__doc__)
         sys.exit(2)
