@@ -106,6 +106,51 @@ def _bf16(t):
     return t
 
 
+def _buf(t, dtype, numel: int, name: str, dev):
+    """A caller-provided buffer the library writes or reads as a flat array:
+    a contiguous tensor of `dtype` on the operands' device with at least
+    `numel` elements (the C side sees only its address).  None passes."""
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a tensor on {dev}")
+    return t
+
+
+def _ws_bytes(t, dev) -> int:
+    """Size in bytes of a caller's workspace tensor (any dtype, contiguous,
+    on the operands' device); 0 for None."""
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"workspace must be a tensor on {dev}")
+    return t.numel() * t.element_size()
+
+
+def _kept_bufs(kept_blocks, n_kept, dev_status, dev):
+    """The kept-block list (int32, read up to the device-side count), the
+    count (int32[1]) and the optional status word (int32[1])."""
+    if kept_blocks is None or n_kept is None:
+        raise ValueError("kept_blocks and n_kept are required")
+    _buf(kept_blocks, torch.int32, 0, "kept_blocks", dev)
+    _buf(n_kept, torch.int32, 1, "n_kept", dev)
+    _buf(dev_status, torch.int32, 1, "dev_status", dev)
+
+
+def _rows_within(t, n_rows: int, width: int, name: str):
+    """n_rows x width must lie inside the 2-D tensor t."""
+    if n_rows > t.shape[0] or width > t.shape[1]:
+        raise ValueError(f"{name} is {tuple(t.shape)}, {n_rows} x {width} needed")
+
+
 # ---------------------------------------------------------------- calls
 def lemo_block_scores_workspace(n_tokens: int, block: int) -> int:
     return lib().lemo_block_scores_workspace(n_tokens, block)
@@ -116,17 +161,19 @@ def lemo_block_scores(q, k, n_heads: int, head_dim: int, block: int, head_reduce
     """Exact block scores.  Returns (scores [nb] fp32, block_scores [nb][nb] or None)."""
     _bf16(q), _bf16(k)
     n = q.shape[0]
+    if block <= 0:
+        raise ValueError(f"block must be positive (got {block})")
     nb = n // block
+    _rows_within(k, n, 0, "k")
     if scores is None:
         scores = torch.empty(nb, dtype=torch.float32, device=q.device)
-    ws_bytes = 0
-    if block_scores is None:
-        ws_bytes = lemo_block_scores_workspace(n, block)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _buf(scores, torch.float32, nb, "scores", q.device)
+    _buf(block_scores, torch.float32, nb * nb, "block_scores", q.device)
+    if block_scores is None and workspace is None:
+        workspace = torch.empty(max(lemo_block_scores_workspace(n, block), 1), dtype=torch.uint8, device=q.device)
     st = lib().lemo_block_scores(_ptr(q), _ptr(k), n, n_heads, head_dim, _ld(q), _ld(k), block, head_reduce,
                                  _ptr(block_scores), _ptr(scores), _ptr(workspace),
-                                 workspace.numel() if workspace is not None else 0, _stream(q.device))
+                                 _ws_bytes(workspace, q.device), _stream(q.device))
     _check(st, "lemo_block_scores")
     return scores, block_scores
 
@@ -147,18 +194,20 @@ def lemo_block_scores_batched(q, k, n_heads: int, head_dim: int, block: int, hea
     if q.dim() != 3 or k.dim() != 3 or q.shape[:2] != k.shape[:2] or q.stride(2) != 1 or k.stride(2) != 1:
         raise ValueError("q and k must be [B][N][width] with unit column stride and the same B, N")
     B, n = q.shape[0], q.shape[1]
+    if block <= 0:
+        raise ValueError(f"block must be positive (got {block})")
     nb = (n + block - 1) // block
     if scores is None:
         scores = torch.empty(B, nb, dtype=torch.float32, device=q.device)
-    ws_bytes = 0
-    if block_scores is None:
-        ws_bytes = lemo_block_scores_batched_workspace(B, n, block)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _buf(scores, torch.float32, B * nb, "scores", q.device)
+    _buf(block_scores, torch.float32, B * nb * nb, "block_scores", q.device)
+    if block_scores is None and workspace is None:
+        workspace = torch.empty(max(lemo_block_scores_batched_workspace(B, n, block), 1), dtype=torch.uint8,
+                                device=q.device)
     st = lib().lemo_block_scores_batched(_ptr(q), _ptr(k), B, n, n_heads, head_dim, q.stride(1), k.stride(1),
                                          q.stride(0), k.stride(0), block, head_reduce, LEMO_SCORES_CAUSAL if causal else 0,
                                          _ptr(block_scores), _ptr(scores), _ptr(workspace),
-                                         workspace.numel() if workspace is not None else 0, _stream(q.device))
+                                         _ws_bytes(workspace, q.device), _stream(q.device))
     _check(st, "lemo_block_scores_batched")
     return scores, block_scores
 
@@ -175,14 +224,22 @@ def lemo_predict_scores(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, 
     n = x.shape[0]
     d = x.shape[1] if d_model is None else d_model
     rank = u_q.shape[1]
+    if block <= 0:
+        raise ValueError(f"block must be positive (got {block})")
     nb = -(-n // block)                 # a ragged last block counts
+    _rows_within(x, n, d, "x")
+    for name, t, r, c in (("u_q", u_q, d, rank), ("u_k", u_k, d, rank), ("v_q", v_q, rank, rank),
+                          ("v_k", v_k, rank, rank)):
+        _buf(t, t.dtype, r * c, name, x.device)
     if scores is None:
         scores = torch.empty(nb, dtype=torch.float32, device=x.device)
+    _buf(scores, torch.float32, nb, "scores", x.device)
+    _buf(block_scores, torch.float32, nb * nb, "block_scores", x.device)
     if workspace is None:
         workspace = torch.empty(max(lemo_predict_scores_workspace(n, d, block, rank), 1), dtype=torch.uint8,
                                 device=x.device)
     st = lib().lemo_predict_scores(_ptr(x), n, d, _ld(x), block, _ptr(u_q), _ptr(v_q), _ptr(u_k), _ptr(v_k), rank,
-                                   _ptr(block_scores), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                   _ptr(block_scores), _ptr(scores), _ptr(workspace), _ws_bytes(workspace, x.device),
                                    _stream(x.device))
     _check(st, "lemo_predict_scores")
     return scores, block_scores
@@ -207,12 +264,18 @@ def lemo_token_embeddings(x, u_q, v_q, u_k, v_k, d_model: int = None, q_hat=None
     _bf16(q_hat), _bf16(k_hat)
     if _ld(q_hat) != _ld(k_hat):
         raise ValueError("q_hat and k_hat must share a row stride")
+    _rows_within(x, n, d, "x")
+    _rows_within(q_hat, n, rank, "q_hat")
+    _rows_within(k_hat, n, rank, "k_hat")
+    for name, t, r, c in (("u_q", u_q, d, rank), ("u_k", u_k, d, rank), ("v_q", v_q, rank, rank),
+                          ("v_k", v_k, rank, rank)):
+        _buf(t, t.dtype, r * c, name, x.device)
     if workspace is None:
         workspace = torch.empty(max(lemo_token_embeddings_workspace(n, d, rank), 1), dtype=torch.uint8,
                                 device=x.device)
     st = lib().lemo_token_embeddings(_ptr(x), n, d, _ld(x), _ptr(u_q), _ptr(v_q), _ptr(u_k), _ptr(v_k), rank,
-                                     _ptr(q_hat), _ptr(k_hat), _ld(q_hat), _ptr(workspace), workspace.numel(),
-                                     _stream(x.device))
+                                     _ptr(q_hat), _ptr(k_hat), _ld(q_hat), _ptr(workspace),
+                                     _ws_bytes(workspace, x.device), _stream(x.device))
     _check(st, "lemo_token_embeddings")
     return q_hat, k_hat
 
@@ -222,10 +285,16 @@ def lemo_select_mask(scores, mode: int, threshold: float = 0.0, keep_blocks: int
     """Threshold + compaction.  Returns (mask u8, kept_blocks i32, n_kept i32[1], threshold_used f32[1])."""
     nb = scores.shape[0]
     dev = scores.device
+    _buf(scores, torch.float32, nb, "scores", dev)
     mask = torch.empty(nb, dtype=torch.uint8, device=dev) if mask is None else mask
     kept_blocks = torch.empty(nb, dtype=torch.int32, device=dev) if kept_blocks is None else kept_blocks
     n_kept = torch.empty(1, dtype=torch.int32, device=dev) if n_kept is None else n_kept
     threshold_used = torch.empty(1, dtype=torch.float32, device=dev) if threshold_used is None else threshold_used
+    _buf(mask, torch.uint8, nb, "mask", dev)
+    _buf(kept_blocks, torch.int32, nb, "kept_blocks", dev)
+    _buf(n_kept, torch.int32, 1, "n_kept", dev)
+    _buf(threshold_used, torch.float32, 1, "threshold_used", dev)
+    _buf(dev_status, torch.int32, 1, "dev_status", dev)
     st = lib().lemo_select_mask(_ptr(scores), nb, mode, float(threshold), int(keep_blocks), _ptr(mask),
                                 _ptr(kept_blocks), _ptr(n_kept), _ptr(threshold_used), _ptr(dev_status),
                                 _stream(dev))
@@ -239,6 +308,9 @@ def lemo_gather_pad(src, block: int, kept_blocks, n_kept, dst, pad_multiple: int
     _bf16(src), _bf16(dst)
     w = src.shape[1] if width is None else width
     n = src.shape[0] if n_tokens is None else n_tokens
+    _rows_within(src, n, w, "src")
+    _rows_within(dst, 0, w, "dst")
+    _kept_bufs(kept_blocks, n_kept, dev_status, src.device)
     st = lib().lemo_gather_pad(_ptr(src), n, w, _ld(src), block, _ptr(kept_blocks), _ptr(n_kept), _ptr(dst),
                                _ld(dst), dst.shape[0], pad_multiple, _ptr(dev_status), _stream(src.device))
     _check(st, "lemo_gather_pad")
@@ -251,6 +323,9 @@ def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: i
     _bf16(residual), _bf16(y)
     w = residual.shape[1] if width is None else width
     n = residual.shape[0] if n_tokens is None else n_tokens
+    _rows_within(residual, n, w, "residual")
+    _rows_within(y, 0, w, "y")
+    _kept_bufs(kept_blocks, n_kept, dev_status, residual.device)
     st = lib().lemo_scatter_residual(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
                                      _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
     _check(st, "lemo_scatter_residual")
@@ -263,6 +338,9 @@ def lemo_residual_recompute(residual, block: int, kept_blocks, n_kept, y, width:
     _bf16(residual), _bf16(y)
     w = residual.shape[1] if width is None else width
     n = residual.shape[0] if n_tokens is None else n_tokens
+    _rows_within(residual, n, w, "residual")
+    _rows_within(y, 0, w, "y")
+    _kept_bufs(kept_blocks, n_kept, dev_status, residual.device)
     st = lib().lemo_residual_recompute(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
                                        _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
     _check(st, "lemo_residual_recompute")
@@ -276,8 +354,12 @@ def lemo_mlp_block_scores_workspace(n_tokens: int, width: int, block: int) -> in
 def _mlp_out(a, block, width, scores, workspace):
     n = a.shape[0]
     w = a.shape[1] if width is None else width
+    if block <= 0:
+        raise ValueError(f"block must be positive (got {block})")
+    _rows_within(a, n, w, "act")
     if scores is None:
         scores = torch.empty(-(-n // block), dtype=torch.float32, device=a.device)
+    _buf(scores, torch.float32, -(-n // block), "scores", a.device)
     if workspace is None:
         workspace = torch.empty(max(lemo_mlp_block_scores_workspace(n, w, block), 1), dtype=torch.uint8,
                                 device=a.device)
@@ -289,7 +371,7 @@ def lemo_mlp_block_scores(act, block: int, width: int = None, scores=None, works
     _bf16(act)
     n, w, scores, workspace = _mlp_out(act, block, width, scores, workspace)
     st = lib().lemo_mlp_block_scores(_ptr(act), n, w, _ld(act), block, _ptr(scores), _ptr(workspace),
-                                     workspace.numel(), _stream(act.device))
+                                     _ws_bytes(workspace, act.device), _stream(act.device))
     _check(st, "lemo_mlp_block_scores")
     return scores
 
@@ -298,8 +380,9 @@ def lemo_mlp_block_scores_gated(gate, up, block: int, width: int = None, scores=
     """MLP-block token scores of SiLU(gate) * up; returns scores [ceil(N / block)] fp32."""
     _bf16(gate), _bf16(up)
     n, w, scores, workspace = _mlp_out(gate, block, width, scores, workspace)
+    _rows_within(up, n, w, "up")
     st = lib().lemo_mlp_block_scores_gated(_ptr(gate), _ptr(up), n, w, _ld(gate), _ld(up), block, _ptr(scores),
-                                           _ptr(workspace), workspace.numel(), _stream(gate.device))
+                                           _ptr(workspace), _ws_bytes(workspace, gate.device), _stream(gate.device))
     _check(st, "lemo_mlp_block_scores_gated")
     return scores
 
@@ -310,6 +393,10 @@ def lemo_gather_linear(x, block: int, kept_blocks, n_kept, weight, y, pad_multip
     _bf16(x), _bf16(weight), _bf16(y)
     din = x.shape[1] if d_in is None else d_in
     n = x.shape[0] if n_tokens is None else n_tokens
+    _rows_within(x, n, din, "x")
+    _rows_within(weight, 0, din, "weight")
+    _rows_within(y, 0, weight.shape[0], "y")
+    _kept_bufs(kept_blocks, n_kept, dev_status, x.device)
     st = lib().lemo_gather_linear(_ptr(x), n, din, _ld(x), block, _ptr(kept_blocks), _ptr(n_kept), _ptr(weight),
                                   weight.shape[0], _ld(weight), _ptr(y), _ld(y), y.shape[0], pad_multiple,
                                   _ptr(dev_status), _stream(x.device))
@@ -321,6 +408,10 @@ def lemo_linear_scatter(a, weight, residual, block: int, kept_blocks, n_kept, d_
     """In-place addition fused into a product: residual[token(p)] += bf16(a[p] weightᵀ)."""
     _bf16(a), _bf16(weight), _bf16(residual)
     din = a.shape[1] if d_in is None else d_in
+    _rows_within(a, 0, din, "a")
+    _rows_within(weight, 0, din, "weight")
+    _rows_within(residual, 0, weight.shape[0], "residual")
+    _kept_bufs(kept_blocks, n_kept, dev_status, a.device)
     st = lib().lemo_linear_scatter(_ptr(a), din, _ld(a), a.shape[0], _ptr(weight), weight.shape[0], _ld(weight),
                                    _ptr(residual), residual.shape[0], _ld(residual), block, _ptr(kept_blocks),
                                    _ptr(n_kept), _ptr(dev_status), _stream(a.device))

@@ -295,3 +295,30 @@ def test_launch_grid_limits(L):
                flags=0) == UNSUP
     assert ps(L, n=65536 * 2 + 2, b=2, ws=NULL) == UNSUP
     assert ps(L, n=65535 * 2, b=2, ws=NULL) == WS
+
+
+def test_binding_buffer_checks():
+    """The binding refuses buffers the C side could not tell apart from good
+    ones (it sees only an address): wrong dtype, host memory, non-contiguous,
+    too small.  Host-side checks only; no call reaches the library."""
+    import torch
+    t = torch.zeros(8, dtype=torch.float32)
+    gpu = torch.device("cuda", 0)
+    with pytest.raises(TypeError):
+        lemo._buf(torch.zeros(8, dtype=torch.float64), torch.float32, 8, "scores", gpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        lemo._buf(torch.zeros(4, 4)[:, 1], torch.float32, 4, "scores", gpu)
+    with pytest.raises(ValueError, match="9 needed"):
+        lemo._buf(t, torch.float32, 9, "scores", gpu)
+    with pytest.raises(ValueError, match="tensor on"):      # host memory
+        lemo._buf(t, torch.float32, 8, "scores", gpu)
+    assert lemo._buf(None, torch.float32, 9, "scores", gpu) is None
+    with pytest.raises(ValueError, match="contiguous"):
+        lemo._ws_bytes(torch.zeros(4, 4)[:, 1], gpu)
+    with pytest.raises(ValueError, match="tensor on"):
+        lemo._ws_bytes(t, gpu)
+    assert lemo._ws_bytes(None, gpu) == 0
+    with pytest.raises(ValueError, match="16 x 4 needed"):
+        lemo._rows_within(torch.zeros(8, 4), 16, 4, "x")
+    with pytest.raises(ValueError, match="required"):
+        lemo._kept_bufs(None, None, None, t.device)

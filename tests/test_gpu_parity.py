@@ -1121,3 +1121,29 @@ def test_fused_full_size_sampled():
                              O.linear_bf16(a[sample], wq))
     ok, same = _embeddings_close(res[rows[sample]], ref)
     assert ok, same
+
+
+def test_binding_rejects_bad_buffers():
+    """Buffers the library would write through blindly are refused before any
+    launch: host memory, a wrong dtype, too few elements.  A float32
+    workspace is counted in bytes."""
+    n, h, hd, b = 256, 2, 64, 64
+    rng = np.random.default_rng(11)
+    qn, kn = synth.random_bf16(rng, (n, h * hd)), synth.random_bf16(rng, (n, h * hd))
+    q, k = dev(qn), dev(kn)
+    nb = n // b
+    with pytest.raises(ValueError, match="tensor on"):
+        lemo.lemo_block_scores(q, k, h, hd, b, scores=torch.zeros(nb))
+    with pytest.raises(TypeError):
+        lemo.lemo_block_scores(q, k, h, hd, b, scores=torch.zeros(nb, dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError, match="needed"):
+        lemo.lemo_block_scores(q, k, h, hd, b, block_scores=torch.zeros(nb, nb - 1, device="cuda"))
+    with pytest.raises(ValueError, match="needed"):
+        lemo.lemo_select_mask(torch.zeros(nb, device="cuda"), lemo.SELECT_MEAN,
+                              kept_blocks=torch.zeros(nb - 1, dtype=torch.int32, device="cuda"))
+    # the workspace holds nb*nb floats: a float32 tensor of that many elements suffices
+    ws = torch.empty(lemo.lemo_block_scores_workspace(n, b) // 4, dtype=torch.float32, device="cuda")
+    I, _ = lemo.lemo_block_scores(q, k, h, hd, b, workspace=ws)
+    M_ref, I_ref = O.exact_block_scores(qn, kn, h, hd, b, O.REDUCE_PAPER)
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok, worst
