@@ -372,7 +372,9 @@ def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
     mask: the kept-row gather feeding a d x d projection (lemo_gather_linear)
     and a d x d projection added back into the residual stream
     (lemo_linear_scatter), each against the stand-alone movement call plus the
-    same product.  Mean event times over `reps` calls after 3 warm-up calls."""
+    same product, and the gather against the stand-alone gather plus the vendor
+    library's product (torch.mm, hipBLASLt) as a reference point.  Mean event
+    times over `reps` calls after a clock-settle phase."""
     import torch
     from contextual_token_sparsity_amd import lemo
     R = nk * b
@@ -392,6 +394,14 @@ def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
         lemo.lemo_gather_pad(x, b, kept, n_kept, xg, pad_multiple=256)
         lemo.lemo_gather_linear(xg, b, ident, n_kept, w, y, pad_multiple=256, n_tokens=cap)
 
+    xgb = xg.view(torch.bfloat16)
+    yb = torch.empty((cap, d), dtype=torch.bfloat16, device=dev)
+    wt = w.t().contiguous()                     # [in][out]: a plain row-major product
+
+    def gather_then_library():
+        lemo.lemo_gather_pad(x, b, kept, n_kept, xg, pad_multiple=256)
+        torch.mm(xgb, wt, out=yb)
+
     def scatter_fused():
         lemo.lemo_linear_scatter(a[:R], w, resid, b, kept, n_kept)
 
@@ -401,6 +411,7 @@ def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
 
     res = {}
     for name, fn in (("gather_linear", gather_fused), ("gather_then_linear", gather_unfused),
+                     ("gather_then_library_linear", gather_then_library),
                      ("linear_scatter", scatter_fused), ("linear_then_scatter", scatter_unfused)):
         _settle(fn)
         e0 = torch.cuda.Event(enable_timing=True)
