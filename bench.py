@@ -228,6 +228,7 @@ def main():
                     "cold_frac": move_bytes_k[kname] / (cold_ms[kname] * 1e-3) / 1e9 / PEAK_HBM_GBS}
             for kname in ("gather_x", "gather_act", "scatter")},
         "predictor_path_tokens_per_s": N / (sum(v for kk, v in stages.items() if kk != "block_scores") * 1e-3),
+        "tokens_per_s_without_mlp_gather": N / ((ms_step - warm_ms["gather_act"]) * 1e-3),
         "dev_status": st,
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
@@ -237,6 +238,7 @@ def main():
     out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
+    out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -291,6 +293,31 @@ def causal_scores(q, k, N, H, hd, b, mode, stream, dev, reps=10):
     tf = flops / (t * 1e-3) / 1e12
     return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3),
             "traffic": load_traffic(causal=True) if mode == lemo.REDUCE_PAPER else None}
+
+
+def exact_scores_other_configs(mode, stream, dev):
+    """The exact scores at the two smaller exact-scoring configurations
+    (Llama2-7B at N = 8192, and OPT-1.3B at N = 4096 with 32 heads of 64),
+    on seeded random bf16 Q and K of those shapes (the work does not depend on
+    the values): mean event time of 10 calls after a clock-settle phase, flops
+    2 N^2 hd H, and the fraction of the bf16 peak."""
+    import torch
+    from contextual_token_sparsity_amd import lemo, synth
+    res = {}
+    for name in ("llama2-7b-n8k-exact", "opt1.3b-n4k"):
+        w = synth.WORKLOADS[name]
+        N, H, hd, b = w.n_tokens, w.n_heads, w.head_dim, w.block
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        q = torch.randn(N, H * hd, device=dev, generator=g).to(torch.bfloat16)
+        k = torch.randn(N, H * hd, device=dev, generator=g).to(torch.bfloat16)
+        I = torch.empty(N // b, dtype=torch.float32, device=dev)
+        ws = torch.empty(lemo.lemo_block_scores_workspace(N, b), dtype=torch.uint8, device=dev)
+        t = _mean_ms(lambda: lemo.lemo_block_scores(q, k, H, hd, b, mode, scores=I, workspace=ws), stream)
+        tf = 2.0 * N * N * hd * H / (t * 1e-3) / 1e12
+        res[name] = {"n_tokens": N, "n_heads": H, "head_dim": hd, "block": b, "ms": t, "TFLOPs": tf,
+                     "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3)}
+        del q, k, ws
+    return res
 
 
 def _mean_ms(fn, stream, reps=10, warm=3):
