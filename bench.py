@@ -234,6 +234,7 @@ def main():
         "clock_settle_steps": settle_steps,
     }
     out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
+    out["other_head_reduce"] = other_head_reduce(q, k, N, H, hd, b, mode, stream, dev)
     out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
     out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
@@ -293,6 +294,21 @@ def causal_scores(q, k, N, H, hd, b, mode, stream, dev, reps=10):
     tf = flops / (t * 1e-3) / 1e12
     return {"ms": t, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3),
             "traffic": load_traffic(causal=True) if mode == lemo.REDUCE_PAPER else None}
+
+
+def other_head_reduce(q, k, N, H, hd, b, mode, stream, dev):
+    """The exact scores with the other head reduction (HEADMAX when the step
+    uses PAPER, and the reverse) on the same Q and K: mean event time of 10
+    calls after a clock-settle phase, TFLOP/s and fraction of the bf16 peak."""
+    import torch
+    from contextual_token_sparsity_amd import lemo
+    other = lemo.REDUCE_HEADMAX if mode == lemo.REDUCE_PAPER else lemo.REDUCE_PAPER
+    I = torch.empty(N // b, dtype=torch.float32, device=dev)
+    ws = torch.empty(lemo.lemo_block_scores_workspace(N, b), dtype=torch.uint8, device=dev)
+    t = _mean_ms(lambda: lemo.lemo_block_scores(q, k, H, hd, b, other, scores=I, workspace=ws), stream)
+    tf = 2.0 * N * N * hd * H / (t * 1e-3) / 1e12
+    return {"head_reduce": "headmax" if other == lemo.REDUCE_HEADMAX else "paper", "ms": t, "TFLOPs": tf,
+            "frac": tf / PEAK_BF16_TFLOPS, "tokens_per_s": N / (t * 1e-3)}
 
 
 def exact_scores_other_configs(mode, stream, dev):
