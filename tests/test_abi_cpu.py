@@ -322,3 +322,23 @@ def test_binding_buffer_checks():
         lemo._rows_within(torch.zeros(8, 4), 16, 4, "x")
     with pytest.raises(ValueError, match="required"):
         lemo._kept_bufs(None, None, None, t.device)
+
+
+def test_last_error_is_per_thread(L):
+    """The detail text of a failed call belongs to the calling thread: two
+    threads that fail differently each read back their own message."""
+    import threading
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def run(name, kw):
+        st = bs(L, **kw)
+        barrier.wait()                      # both calls have failed before either reads
+        seen[name] = (st, lemo.lemo_last_error())
+
+    t1 = threading.Thread(target=run, args=("n", dict(n=1000)))
+    t2 = threading.Thread(target=run, args=("mode", dict(mode=2)))
+    t1.start(), t2.start()
+    t1.join(), t2.join()
+    assert seen["n"][0] == INVALID and "not a multiple" in seen["n"][1]
+    assert seen["mode"][0] == INVALID and "head_reduce" in seen["mode"][1]

@@ -1147,3 +1147,54 @@ def test_binding_rejects_bad_buffers():
     M_ref, I_ref = O.exact_block_scores(qn, kn, h, hd, b, O.REDUCE_PAPER)
     ok, worst = scores_close(I.cpu().numpy(), I_ref)
     assert ok, worst
+
+
+def test_concurrent_streams_match_sequential():
+    """Calls are thread-safe: two host threads, each on its own stream, run the
+    exact scores, the predictor, select and gather on their own buffers while
+    the other does the same; every output equals, bit for bit, the output of
+    the same calls made one after the other."""
+    import threading
+    n, h, hd, b, d, r = 1024, 4, 128, 64, 512, 64
+    nb = n // b
+
+    def inputs(seed):
+        q, k = rand_qk(seed, n, h, hd)
+        x, w = _pred_inputs(seed + 1, n, d, r)
+        return [dev(q), dev(k), dev(x)] + [dev(a) for a in w]
+
+    def run(t):
+        q, k, x, uq, vq, uk, vk = t
+        I, _ = lemo.lemo_block_scores(q, k, h, hd, b)
+        Ip, _ = lemo.lemo_predict_scores(x, uq, vq, uk, vk, b)
+        mask, kept, nk, _ = lemo.lemo_select_mask(Ip, lemo.SELECT_TOPK, keep_blocks=nb // 2)
+        dst = torch.zeros((n, d), dtype=torch.int16, device="cuda")
+        lemo.lemo_gather_pad(x, b, kept, nk, dst, pad_multiple=64)
+        return [I, Ip, mask, kept, dst]
+
+    ins = [inputs(101), inputs(202)]
+    ref = [run(t) for t in ins]
+    torch.cuda.synchronize()
+    ref = [[a.cpu() for a in r_] for r_ in ref]
+
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    barrier = threading.Barrier(2)
+
+    def worker(i):
+        with torch.cuda.stream(streams[i]):
+            barrier.wait()
+            out = None
+            for _ in range(4):
+                out = run(ins[i])
+            streams[i].synchronize()
+            got[i] = [a.cpu() for a in out]
+
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    for i in range(2):
+        for a, r_ in zip(got[i], ref[i]):
+            assert torch.equal(a, r_)
