@@ -29,7 +29,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls only enqueue work; they never synchronise.  Outputs are valid once
  *    the stream reaches them.  Device-resident results (n_kept, kept_blocks)
- *    flow device-to-device between calls without a host round trip.
+ *    flow device-to-device between calls without a host round trip.  A call
+ *    enqueues kernel launches only (no allocation, memset or copy), so a
+ *    sequence of calls can be captured in a HIP graph and replayed.
  *  - Arguments are validated on the host BEFORE anything is enqueued: a
  *    non-OK status means nothing was launched.  lemo_last_error() gives a
  *    thread-local text for the last non-OK status.  A failing launch returns
