@@ -226,6 +226,37 @@ def test_scores_batched_small(shape, mode, causal):
         assert not Mg[:, np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]].any()
 
 
+ONE_HEAD_WALK = [
+    # (B, N, hd, block, causal): one head, more than 2048 tiles in the launch,
+    # so each workgroup walks a range of several tiles (the next tile's first
+    # chunk loading under the current tile's last)
+    (1, 6144, 64, 128, False),     # 128-row blocks: the four waves' maxima meet in LDS per tile
+    (1, 6144, 128, 32, False),     # 32-row blocks: each wave writes its own four blocks
+    (2, 6000, 128, 64, False),     # batch of two ragged sequences
+    (1, 8190, 64, 64, True),       # causal, ragged: 2080 tiles on or below the diagonal
+]
+
+
+@pytest.mark.parametrize("shape", ONE_HEAD_WALK, ids=lambda s: "B%d_N%d_hd%d_b%d_%s" % (*s[:4], "causal" if s[4] else "full"))
+def test_one_head_range_walk(shape):
+    """The one-head kernel (the per-token predictor's scoring) when every
+    workgroup walks several consecutive tiles: the whole block matrix against
+    the oracle."""
+    B, n, hd, b, causal = shape
+    say("one-head range walk", shape)
+    q, k = rand_batch(4000 + n + hd, B, n, 1, hd)
+    M_ref, I_ref = O.exact_block_scores_batched(q, k, 1, hd, b, O.REDUCE_PAPER, causal=causal)
+    nb = -(-n // b)
+    M = torch.full((B, nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), 1, hd, b, O.REDUCE_PAPER, causal=causal, block_scores=M)
+    torch.cuda.synchronize()
+    Mg, Ig = M.cpu().numpy(), I.cpu().numpy()
+    assert (Mg >= 0).all()
+    okm, worstm = scores_close(Mg, M_ref)
+    ok, worst = scores_close(Ig, I_ref)
+    assert okm and ok and worstm < 1e-4 and worst < 1e-4, (worstm, worst)
+
+
 def test_scores_batched_equals_single_call():
     """One sequence, whole blocks, no mask: the same kernel as lemo_block_scores, bit for bit."""
     q, k = rand_qk(41, 1024, 4, 128)
