@@ -342,3 +342,12 @@ def test_last_error_is_per_thread(L):
     t1.join(), t2.join()
     assert seen["n"][0] == INVALID and "not a multiple" in seen["n"][1]
     assert seen["mode"][0] == INVALID and "head_reduce" in seen["mode"][1]
+
+
+def test_headmax_head_limit(L):
+    """HEADMAX keeps per-head maxima for at most 128 heads: 129 are refused;
+    PAPER has no such limit (this call stops at the missing workspace)."""
+    assert bs(L, h=129, hd=64, ldq=129 * 64, ldk=129 * 64, mode=1) == UNSUP
+    assert "128 heads" in lemo.lemo_last_error()
+    assert bs(L, h=128, hd=64, ldq=128 * 64, ldk=128 * 64, mode=1, M=NULL, ws=NULL) == WS
+    assert bs(L, h=129, hd=64, ldq=129 * 64, ldk=129 * 64, mode=0, M=NULL, ws=NULL) == WS

@@ -68,6 +68,24 @@ def test_exact_small(shape, mode):
     assert worst < 1e-4 and worstm < 1e-4, (worst, worstm)   # fp32 accumulation, not 1e-2
 
 
+@pytest.mark.parametrize("block", [32, 64, 128])
+def test_headmax_most_heads(block):
+    """HEADMAX at its largest head count (128): with 128-row blocks every
+    head's per-wave maxima are kept in LDS and summed in head order at the end
+    of the tile; 32- and 64-row blocks sum in registers."""
+    n, h, hd = 384, 128, 64
+    say("headmax most heads", n, h, hd, block)
+    q, k = rand_qk(5100 + block, n, h, hd)
+    M_ref, I_ref = O.exact_block_scores(q, k, h, hd, block, O.REDUCE_HEADMAX)
+    nb = n // block
+    M = torch.full((nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_block_scores(dev(q), dev(k), h, hd, block, O.REDUCE_HEADMAX, block_scores=M)
+    torch.cuda.synchronize()
+    okm, worstm = scores_close(M.cpu().numpy(), M_ref)
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert okm and ok and worstm < 1e-4 and worst < 1e-4, (worstm, worst)
+
+
 @pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
 @pytest.mark.parametrize("wname", ["tiny", "opt1.3b-n4k"])
 def test_exact_workload(wname, mode):
