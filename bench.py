@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--head-reduce", choices=["paper", "headmax"], default="paper")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the exact scores at the smaller configurations (they launch the same kernel "
+                         "instantiation as the step, which would mix into a profiler's per-kernel average)")
     return ap.parse_args()
 
 
@@ -239,7 +242,8 @@ def main():
     out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
     out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
-    out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
+    if not args.no_other_configs:
+        out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
