@@ -20,10 +20,10 @@ hipError_t lemo_launch_gather_linear(const uint16_t* x, int n_tokens, int d_in, 
                                      int ld_w, uint16_t* y, int ld_y, int cap_rows, int pad_multiple,
                                      int32_t* dev_status, hipStream_t st) {
   int tm, tn;
-  const dim3 grid = grid_for(128, cap_rows, d_out, 1, tm, tn);
+  const dim3 grid = grid_for(256, 256, cap_rows, d_out, 1, tm, tn);
   const Args g = {{x, x}, {w, w}, {y, y}};
   const RowMap rm = {kept, n_kept, block, n_tokens, pad_multiple, dev_status};
-  hipLaunchKernelGGL((k_gemm_nt<kEpiGather, 128>), grid, dim3(kThreads), 0, st, g, ld_x, ld_w, cap_rows, d_out, d_in,
+  hipLaunchKernelGGL((k_gemm_nt<kEpiGather, 256, 256, 8>), grid, dim3(512), 0, st, g, ld_x, ld_w, cap_rows, d_out, d_in,
                      ld_y, tm, tn, rm);
   return hipGetLastError();
 }
@@ -34,10 +34,10 @@ hipError_t lemo_launch_linear_scatter(const uint16_t* a, int d_in, int ld_a, int
                                       hipStream_t st) {
   int tm, tn;
   const int rows = cap_rows < n_tokens ? cap_rows : n_tokens;
-  const dim3 grid = grid_for(128, rows, d_out, 1, tm, tn);
+  const dim3 grid = grid_for(256, 256, rows, d_out, 1, tm, tn);
   const Args g = {{a, a}, {w, w}, {res, res}};
   const RowMap rm = {kept, n_kept, block, n_tokens, 1, dev_status};
-  hipLaunchKernelGGL((k_gemm_nt<kEpiScatterAdd, 128>), grid, dim3(kThreads), 0, st, g, ld_a, ld_w, rows, d_out, d_in,
+  hipLaunchKernelGGL((k_gemm_nt<kEpiScatterAdd, 256, 256, 8>), grid, dim3(512), 0, st, g, ld_a, ld_w, rows, d_out, d_in,
                      ld_res, tm, tn, rm);
   return hipGetLastError();
 }

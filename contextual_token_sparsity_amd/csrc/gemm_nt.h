@@ -3,15 +3,21 @@
 // Device code shared by the per-token predictor and the fused movement
 // products; each translation unit gets its own copy (internal linkage).
 //
-// One TM x 128 tile of C per workgroup of 4 waves (TM/2 x 64 per wave as
-// TM/64 x 2 v_mfma_f32_32x32x16_bf16 tiles).  TM = 64 suits a narrow B (more
-// workgroups: the predictor's 16384 x 256 hidden layer still spreads over 512);
-// TM = 128 suits a square weight (each operand fragment feeds two MFMAs).  The
-// reduction streams in 64-wide chunks through an LDS ring filled by direct
-// global->LDS loads (3 stages for TM = 64, two chunks in flight; 2 stages for
-// TM = 128, so that two workgroups still fit on a CU), with the 16-byte
-// pieces of each 128-B LDS row XOR-swizzled so that
-// the operand reads are free of bank conflicts.  Workgroup ids go round-robin
+// One TM x TN tile of C per workgroup of WAVES waves in a 2 x (WAVES/2)
+// grid of v_mfma_f32_32x32x16_bf16 tiles:
+//   64 x 128, 4 waves of 32 x 64: a narrow B (more workgroups: the
+//     predictor's 16384 x 256 hidden layer still spreads over 512), 3-stage
+//     ring (two chunks in flight), two workgroups per CU;
+//   256 x 256, 8 waves of 128 x 64: a d x d weight.  Against 128 x 128 tiles
+//     this halves the refill bytes and cuts the operand reads per MFMA by a
+//     quarter; on this power-limited part less data movement per flop means
+//     a higher clock.  2-stage ring (128 KiB), one workgroup (two waves per
+//     SIMD) per CU.
+// The reduction streams in 64-wide chunks through an LDS ring filled by
+// direct global->LDS loads, with the 16-byte pieces of each 128-B LDS row
+// XOR-swizzled so that the operand reads are free of bank conflicts.  The
+// epilogue stages the bf16 tile in LDS (the ring, or a larger buffer when the
+// tile does not fit in it).  Workgroup ids go round-robin
 // over the 8 XCDs; when there are few column tiles (a narrow B, e.g. the
 // predictor's hidden layer), the column tiles of one row block are given to
 // ids on the same XCD, back to back, so the second read of those rows of A
@@ -39,22 +45,30 @@ namespace {
 
 namespace gemm {
 
-constexpr int kTN = 128;                            // tile columns (B rows)
-constexpr int kWaves = 4;                           // 2 x 2 waves of TM/2 x 64
-constexpr int kThreads = kWaves * 64;
+constexpr int kThreads = 256;                       // 4-wave workgroups (64 x 128 tiles)
 constexpr int kChunk = 64;                          // reduction elements per stage
 constexpr int kRowBytes = kChunk * 2;               // 128 B
-constexpr int kRegionB = kTN * kRowBytes;           // 16 KiB
-constexpr int kDmaB = kRegionB / (kThreads * 16);   // 4 loads of 16 B per thread
 
-template <int TM>
+// TM x TN tile per workgroup of WAVES waves in a 2 x (WAVES/2) grid, each
+// wave TM/2 x TN/(WAVES/2) as v_mfma_f32_32x32x16_bf16 tiles
+template <int TM, int TN, int WAVES>
 struct Tile {
-  static constexpr int kRegionA = TM * kRowBytes;             // 8 or 16 KiB
+  static constexpr int kWaves = WAVES;
+  static constexpr int kThr = WAVES * 64;
+  static constexpr int kWN = WAVES / 2;                        // waves along the columns
+  static constexpr int kRegionA = TM * kRowBytes;
+  static constexpr int kRegionB = TN * kRowBytes;
   static constexpr int kStageBytes = kRegionA + kRegionB;
-  static constexpr int kDmaA = kRegionA / (kThreads * 16);    // 2 or 4
-  static constexpr int kStages = TM == 64 ? 3 : 2;            // 72 or 64 KiB: two workgroups per CU
+  static constexpr int kDmaA = kRegionA / (kThr * 16);        // loads of 16 B per thread and chunk
+  static constexpr int kDmaB = kRegionB / (kThr * 16);
+  static constexpr int kStages = TM == 64 ? 3 : 2;
   static constexpr int kDmaPerChunk = kDmaA + kDmaB;
-  static constexpr int kMT = TM / 64;                         // MFMA row tiles per wave
+  static constexpr int kWRows = TM / 2, kWCols = TN / kWN;     // per wave
+  static constexpr int kMT = kWRows / 32, kNT = kWCols / 32;   // MFMA tiles per wave
+  static constexpr int kOcc = TM * TN >= 256 * 256 ? 1 : 2;    // workgroups per CU
+  static constexpr int kLdt = TN + 8;                          // epilogue staging row stride (elements)
+  static constexpr int kRing = kStages * kStageBytes;
+  static constexpr int kLdsBytes = kRing > TM * kLdt * 2 ? kRing : TM * kLdt * 2;
 };
 
 enum { kEpiReluBf16 = 0, kEpiBf16 = 1, kEpiGather = 2, kEpiScatterAdd = 3 };
@@ -90,14 +104,16 @@ struct RowMap {
 // C[m][n] = sum_k A[m][k] B[n][k] for m < M (the row capacity of C for the
 // gather epilogue), n < Nn; K a multiple of 64, Nn and ldc multiples of 8.  Rows of A (B) past the rows
 // in use read a valid row, and their results are dropped.
-template <int EPI, int TM>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ldb, int M, int Nn, int K, int ldc,
-                                                         int tm_count, int tn_count, RowMap rm) {
-  using T = Tile<TM>;
+template <int EPI, int TM, int TN, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, (Tile<TM, TN, WAVES>::kOcc)) void k_gemm_nt(
+    Args g, int lda, int ldb, int M, int Nn, int K, int ldc, int tm_count, int tn_count, RowMap rm) {
+  using T = Tile<TM, TN, WAVES>;
   constexpr int kRegionA = T::kRegionA, kStageBytes = T::kStageBytes, kDmaA = T::kDmaA, kStages = T::kStages;
-  constexpr int kDmaPerChunk = T::kDmaPerChunk, kMT = T::kMT;
-  constexpr int kWM = TM / 2;                        // rows per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t g_tile[kStages * kStageBytes];
+  constexpr int kDmaB = T::kDmaB, kDmaPerChunk = T::kDmaPerChunk, kMT = T::kMT, kNT = T::kNT;
+  constexpr int kWaves = T::kWaves, kThr = T::kThr, kWN = T::kWN;
+  constexpr int kWM = T::kWRows, kWC = T::kWCols;    // rows and columns per wave
+  constexpr int kTN = TN;
+  __shared__ __attribute__((aligned(1024))) uint8_t g_tile[T::kLdsBytes];
   constexpr bool kMapped = EPI == kEpiGather || EPI == kEpiScatterAdd;
   const uint16_t* __restrict__ A = g.a[blockIdx.z];
   const uint16_t* __restrict__ B = g.b[blockIdx.z];
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wq = wave >> 1, wk = wave & 1;
+  const int wq = wave / kWN, wk = wave % kWN;
   const int l32 = lane & 31, hi = lane >> 5;
   const uint32_t lds0 = (uint32_t)(uintptr_t)g_tile;
 
@@ -170,28 +186,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   // physical piece lane%8, which holds logical piece (lane%8) ^ swz(row)
   uint32_t voffA[kDmaA], voffB[kDmaB];
 #pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = (i * kWaves + wave) * 8 + (lane >> 3);
+    const int piece = (lane & 7) ^ swz(r);
+    int arow;
+    if (EPI == kEpiGather) {
+      const int t = m0 + r < R ? tok_of(m0 + r) : -1;
+      arow = t >= 0 ? t : 0;
+    } else {
+      arow = min(m0 + r, rows_used - 1);
+    }
+    voffA[i] = (uint32_t)(((size_t)arow * lda + piece * 8) * 2);
+  }
+#pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
     const int r = (i * kWaves + wave) * 8 + (lane >> 3);
     const int piece = (lane & 7) ^ swz(r);
-    if (i < kDmaA) {
-      int arow;
-      if (EPI == kEpiGather) {
-        const int t = m0 + r < R ? tok_of(m0 + r) : -1;
-        arow = t >= 0 ? t : 0;
-      } else {
-        arow = min(m0 + r, rows_used - 1);
-      }
-      voffA[i] = (uint32_t)(((size_t)arow * lda + piece * 8) * 2);
-    }
     voffB[i] = (uint32_t)(((size_t)min(n0 + r, Nn - 1) * ldb + piece * 8) * 2);
   }
   auto issue = [&](int c, int stage) {
     const uint32_t base = lds0 + (uint32_t)(stage * kStageBytes);
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i) {
-      if (i < kDmaA) dma16(A + c * kChunk, voffA[i], base + (uint32_t)((i * kWaves + wave) * 1024));
+    for (int i = 0; i < kDmaA; ++i) dma16(A + c * kChunk, voffA[i], base + (uint32_t)((i * kWaves + wave) * 1024));
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i)
       dma16(B + c * kChunk, voffB[i], base + kRegionA + (uint32_t)((i * kWaves + wave) * 1024));
-    }
   };
 
   // per-lane LDS read offsets for the 4 k-steps of a chunk (operand rows all
@@ -201,23 +220,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   for (int s = 0; s < 4; ++s) {
     const int piece = (2 * s + hi) ^ swz(l32);
     offA[s] = (uint32_t)((wq * kWM + l32) * kRowBytes + piece * 16);
-    offB[s] = (uint32_t)(kRegionA + (wk * 64 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(kRegionA + (wk * kWC + l32) * kRowBytes + piece * 16);
   }
 
-  lemo_f32x16 acc[kMT][2];
+  lemo_f32x16 acc[kMT][kNT];
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNT; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-  lemo_bf16x8 fa[2][kMT], fb[2][2];
+  lemo_bf16x8 fa[2][kMT], fb[2][kNT];
   auto read_frags = [&](int buf, const uint8_t* st, int s) {
 #pragma unroll
     for (int a = 0; a < kMT; ++a)
       fa[buf][a] = *reinterpret_cast<const lemo_bf16x8*>(st + offA[s] + a * 32 * kRowBytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
+    for (int i = 0; i < kNT; ++i)
+      fb[buf][i] = *reinterpret_cast<const lemo_bf16x8*>(st + offB[s] + i * 32 * kRowBytes);
   };
 
   const int nchunks = K / kChunk;
@@ -250,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
 #pragma unroll
       for (int a = 0; a < kMT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kNT; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], acc[a][b], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -258,23 +278,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
 
   // epilogue: the bf16 tile is staged in LDS (the ring is free once every
   // wave is past the last chunk), then written with 16-byte row accesses
-  constexpr int kLdt = kTN + 8;                      // LDS row stride (elements)
-  static_assert(TM * kLdt * 2 <= kStages * kStageBytes, "staging tile fits the ring");
+  constexpr int kLdt = T::kLdt;                      // LDS row stride (elements)
   asm volatile("s_barrier" ::: "memory");
   uint16_t* stile = reinterpret_cast<uint16_t*>(g_tile);
 #pragma unroll
   for (int a = 0; a < kMT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNT; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float v = acc[a][b][e];
         if (EPI == kEpiReluBf16) v = fmaxf(v, 0.f);
-        stile[(wq * kWM + a * 32 + acc_row(lane, e)) * kLdt + wk * 64 + b * 32 + l32] = (uint16_t)lemo_f32_to_bf16(v);
+        stile[(wq * kWM + a * 32 + acc_row(lane, e)) * kLdt + wk * kWC + b * 32 + l32] = (uint16_t)lemo_f32_to_bf16(v);
       }
   __syncthreads();
   constexpr int kPieces = kTN / 8;                   // 16-byte pieces per tile row
-  for (int idx = tid; idx < TM * kPieces; idx += kThreads) {
+  for (int idx = tid; idx < TM * kPieces; idx += kThr) {
     const int r = idx / kPieces, c8 = idx % kPieces;
     const int row = m0 + r, col = n0 + c8 * 8;
     if (row >= rows_used || col >= Nn) continue;
@@ -313,10 +332,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_nt(Args g, int lda, int ld
   }
 }
 
-// Grid of k_gemm_nt<., TM>: row tiles x column tiles, products in z.
-inline dim3 grid_for(int tile_rows, int rows, int cols, int products, int& tm_count, int& tn_count) {
+// Grid of k_gemm_nt<., TM, TN, WAVES>: row tiles x column tiles, products in z.
+inline dim3 grid_for(int tile_rows, int tile_cols, int rows, int cols, int products, int& tm_count, int& tn_count) {
   tm_count = (rows + tile_rows - 1) / tile_rows;
-  tn_count = (cols + kTN - 1) / kTN;
+  tn_count = (cols + tile_cols - 1) / tile_cols;
   return dim3(tm_count * tn_count, 1, products);
 }
 

@@ -89,14 +89,14 @@ hipError_t lemo_launch_token_embed(const uint16_t* x, int n_tokens, int d_model,
   // hidden layer: one product, X against [U_q | U_k]^T
   int tm, tn;
   const RowMap none = {nullptr, nullptr, 1, 0, 1, nullptr};
-  const dim3 gh_grid = grid_for(64, n_tokens, r2, 1, tm, tn);
+  const dim3 gh_grid = grid_for(64, 128, n_tokens, r2, 1, tm, tn);
   Args gh = {{x, x}, {ut, ut}, {hid, hid}};
-  hipLaunchKernelGGL((k_gemm_nt<kEpiReluBf16, 64>), gh_grid, dim3(kThreads), 0, st, gh, ld_x, d_model, n_tokens, r2,
+  hipLaunchKernelGGL((k_gemm_nt<kEpiReluBf16, 64, 128, 4>), gh_grid, dim3(kThreads), 0, st, gh, ld_x, d_model, n_tokens, r2,
                      d_model, r2, tm, tn, none);
   // output layer: the query and key products in one launch
-  const dim3 go_grid = grid_for(64, n_tokens, rank, 2, tm, tn);
+  const dim3 go_grid = grid_for(64, 128, n_tokens, rank, 2, tm, tn);
   Args go = {{hid, hid + rank}, {vt, vt + (size_t)rank * rank}, {q_hat, k_hat}};
-  hipLaunchKernelGGL((k_gemm_nt<kEpiBf16, 64>), go_grid, dim3(kThreads), 0, st, go, r2, rank, n_tokens, rank, rank,
+  hipLaunchKernelGGL((k_gemm_nt<kEpiBf16, 64, 128, 4>), go_grid, dim3(kThreads), 0, st, go, r2, rank, n_tokens, rank, rank,
                      ld_out, tm, tn, none);
   return hipGetLastError();
 }
