@@ -539,6 +539,11 @@ def check_select(o) -> list:
     mask, kept, nk, th = o.select_mask(m8, o.SELECT_MEAN)
     _fail(out, th == np.float32(np.mean(m8.astype(np.float64))), "mean threshold")
     _fail(out, np.array_equal(mask.astype(bool), m8 >= th), "mean mask")
+    # mean of scores that are not exact: the correctly rounded sum (math.fsum)
+    # over nb, rounded to float32
+    mask, kept, nk, th = o.select_mask(s, o.SELECT_MEAN)
+    _fail(out, th == np.float32(math.fsum(float(v) for v in s) / s.size), "mean threshold (fsum)")
+    _fail(out, np.array_equal(mask.astype(bool), s >= th), "mean mask (fsum)")
     # random: kept list ascending, counts add up, every kept >= every dropped (topk)
     mask, kept, nk, th = o.select_mask(s, o.SELECT_TOPK, keep_blocks=11)
     _fail(out, np.all(np.diff(kept) > 0) and nk + int((mask == 0).sum()) == s.size, "kept list shape")
@@ -729,7 +734,63 @@ def check_ragged_tail(o) -> list:
     return out
 
 
-ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce,
+def check_exact_column(o) -> list:
+    """exact_column_score(m), the one-column form used by the sampled checks at
+    full size, against the hand examples' column m (E1, E2, E7 and E8, both
+    modes, with and without the causal mask) and against the pure-Python brute
+    force on random tiny full, causal and ragged inputs: I[m] and the column
+    M[:, m] must both match."""
+    out = []
+    g = golden()
+
+    def cmp(q, k, H, hd, b, mode, causal, M_ref, I_ref, what):
+        M_ref, I_ref = np.asarray(M_ref, np.float64), np.asarray(I_ref, np.float64)
+        for m in range(I_ref.shape[0]):
+            val, col = o.exact_column_score(q, k, H, hd, b, mode, m, causal=causal)
+            _fail(out, np.shape(col) == (M_ref.shape[0],) and np.allclose(col, M_ref[:, m], rtol=1e-12, atol=1e-12)
+                  and math.isclose(val, I_ref[m], rel_tol=1e-12, abs_tol=1e-12),
+                  f"column {m} of {what} mode {mode} causal {causal}: {val} {np.asarray(col).tolist()}")
+
+    e1 = g["E1_diagonal_exclusion"]
+    q, k = f2bits(np.array(e1["q"])[:, None]), f2bits(np.array(e1["k"])[:, None])
+    for mode, key in ((o.REDUCE_PAPER, "M_paper"), (o.REDUCE_HEADMAX, "M_headmax")):
+        cmp(q, k, 1, 1, 2, mode, False, e1[key], e1["I"], "E1")
+    e2 = g["E2_head_reduction_order"]
+    q, k = _heads_to_bits(e2["q_heads"]), _heads_to_bits(e2["k_heads"])
+    cmp(q, k, 2, 1, 2, o.REDUCE_PAPER, False, e2["M_paper"], e2["I_paper"], "E2")
+    cmp(q, k, 2, 1, 2, o.REDUCE_HEADMAX, False, e2["M_headmax"], e2["I_headmax"], "E2")
+    e7 = g["E7_causal"]
+    one = e7["one_head"]
+    q, k = f2bits(np.array(one["q"])[:, None]), f2bits(np.array(one["k"])[:, None])
+    for mode in (o.REDUCE_PAPER, o.REDUCE_HEADMAX):
+        cmp(q, k, 1, 1, 2, mode, True, one["M"], one["I"], "E7 one head")
+    two = e7["two_heads"]
+    q, k = _heads_to_bits(two["q_heads"]), _heads_to_bits(two["k_heads"])
+    cmp(q, k, 2, 1, 2, o.REDUCE_PAPER, True, two["M_paper"], two["I_paper"], "E7 two heads")
+    cmp(q, k, 2, 1, 2, o.REDUCE_HEADMAX, True, two["M_headmax"], two["I_headmax"], "E7 two heads")
+    e8 = g["E8_tail_block"]
+    q, k = f2bits(np.array(e8["q"])[:, None]), f2bits(np.array(e8["k"])[:, None])
+    for causal, mk, ik in ((False, "M", "I"), (True, "M_causal", "I_causal")):
+        for mode in (o.REDUCE_PAPER, o.REDUCE_HEADMAX):
+            cmp(q, k, 1, 1, 2, mode, causal, e8[mk], e8[ik], "E8")
+    for s in range(4):
+        rng = np.random.default_rng(500 + s)
+        H = int(rng.integers(1, 4))
+        hd = int(rng.choice([1, 2, 4]))
+        b = int(rng.choice([2, 4]))
+        nb = int(rng.integers(2, 5))
+        tail = int(rng.integers(1, b))
+        for N, causal in ((nb * b, False), (nb * b, True), (nb * b - b + tail, False), (nb * b - b + tail, True)):
+            qf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
+            kf32 = rng.standard_normal((N, H * hd)).astype(np.float32)
+            q, k = torch_bf16_bits(qf32), torch_bf16_bits(kf32)
+            for mode in (0, 1):
+                Mb, Ib = brute_exact(o.bf16_decode(q).tolist(), o.bf16_decode(k).tolist(), H, hd, b, mode, causal)
+                cmp(q, k, H, hd, b, mode, causal, Mb, Ib, f"random seed {s} H{H} hd{hd} b{b} N{N}")
+    return out
+
+
+ALL_CHECKS = [check_bf16_round, check_bf16_add, check_exact_hand, check_exact_bruteforce, check_exact_column,
               check_exact_closed_form, check_exact_invariants, check_predictor, check_token_predictor,
               check_select, check_movement, check_fused_movement, check_mlp_scores, check_recompute,
               check_ragged_tail]

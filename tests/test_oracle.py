@@ -51,6 +51,12 @@ MUTATIONS = [
      [P.check_exact_invariants]),
     ("transposed_column_sum", "I = M.sum(axis=0) if query_blocks", "I = M.sum(axis=1) if query_blocks",
      [P.check_exact_hand]),
+    ("column_takes_query_block", "key_blocks=[key_block], query_blocks=None, causal=causal)",
+     "query_blocks=[key_block], key_blocks=None, causal=causal)", [P.check_exact_column]),
+    ("column_ignores_causal", "key_blocks=[key_block], query_blocks=None, causal=causal)",
+     "key_blocks=[key_block], query_blocks=None, causal=False)", [P.check_exact_column]),
+    ("column_sums_first_row", "return float(M[:, 0].sum()), M[:, 0]", "return float(M[0].sum()), M[:, 0]",
+     [P.check_exact_column]),
     ("no_sqrt_scale", "scale = 1.0 / math.sqrt(head_dim)", "scale = 1.0", [P.check_exact_closed_form]),
     ("no_head_mean", ".sum(axis=0) / n_heads", ".sum(axis=0)", [P.check_exact_closed_form, P.check_exact_hand]),
     ("max_before_clamp_swapped", "M[a] = np.maximum(per_head, 0.0).sum(axis=0)", "M[a] = np.maximum(per_head.sum(axis=0), 0.0)",
