@@ -1,5 +1,6 @@
 // Host side of the C ABI: argument validation (before anything is enqueued),
 // workspace sizing, status strings and the thread-local error text.
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -77,6 +78,9 @@ int lemo_version(void) { return 100; }  // 0.1.0
 // takes at most 2^23 tiles (one head: the workgroups walk ranges of tiles).
 constexpr int kMaxScoreTokens = 1 << 22;
 constexpr long long kMaxWorkgroups = 1LL << 23;
+// The fused products launch one workgroup of 512 work-items per 256 x 256
+// tile of the output.
+constexpr long long kMaxFusedWorkgroups = ((1LL << 31) - 1) / 512;
 
 size_t lemo_block_scores_workspace(int n_tokens, int block) {
   if (n_tokens <= 0 || block <= 0 || n_tokens % block) return 0;
@@ -276,34 +280,50 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
                        "lemo_gather_pad launch");
 }
 
-lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+// The scatter and the recompute: y holds y_rows rows (INT_MAX: the caller
+// guarantees at least the kept rows).
+static lemo_status scatter_common(const char* fn, lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
                                   const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y, int ld_y,
-                                  int32_t* dev_status, void* stream) {
+                                  int y_rows, int32_t* dev_status, void* stream, bool subtract) {
   REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
   REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
+  REQUIRE(y_rows >= 0, LEMO_ERR_INVALID_ARG, "y_rows must not be negative (got %d)", y_rows);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   lemo_status st;
   if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
   if ((st = check_rows(y, ld_y, width, "y")) != LEMO_OK) return st;
   return device_status(lemo_launch_scatter(residual, n_tokens, width, ld_res, block, kept_blocks, n_kept, y, ld_y,
-                                           dev_status, static_cast<hipStream_t>(stream)),
-                       "lemo_scatter_residual launch");
+                                           y_rows, dev_status, static_cast<hipStream_t>(stream), subtract),
+                       fn);
+}
+
+lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                  const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y, int ld_y,
+                                  int32_t* dev_status, void* stream) {
+  return scatter_common("lemo_scatter_residual launch", residual, n_tokens, width, ld_res, block, kept_blocks, n_kept,
+                        y, ld_y, INT_MAX, dev_status, stream, false);
+}
+
+lemo_status lemo_scatter_residual_capped(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                         const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y,
+                                         int ld_y, int y_rows, int32_t* dev_status, void* stream) {
+  return scatter_common("lemo_scatter_residual_capped launch", residual, n_tokens, width, ld_res, block, kept_blocks,
+                        n_kept, y, ld_y, y_rows, dev_status, stream, false);
 }
 
 lemo_status lemo_residual_recompute(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
                                    const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y, int ld_y,
                                    int32_t* dev_status, void* stream) {
-  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
-  REQUIRE(n_tokens > 0 && block > 0 && width > 0, LEMO_ERR_INVALID_ARG,
-          "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
-  REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
-  lemo_status st;
-  if ((st = check_rows(residual, ld_res, width, "residual")) != LEMO_OK) return st;
-  if ((st = check_rows(y, ld_y, width, "y")) != LEMO_OK) return st;
-  return device_status(lemo_launch_scatter(residual, n_tokens, width, ld_res, block, kept_blocks, n_kept, y, ld_y,
-                                           dev_status, static_cast<hipStream_t>(stream), true),
-                       "lemo_residual_recompute launch");
+  return scatter_common("lemo_residual_recompute launch", residual, n_tokens, width, ld_res, block, kept_blocks,
+                        n_kept, y, ld_y, INT_MAX, dev_status, stream, true);
+}
+
+lemo_status lemo_residual_recompute_capped(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                          const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y,
+                                          int ld_y, int y_rows, int32_t* dev_status, void* stream) {
+  return scatter_common("lemo_residual_recompute_capped launch", residual, n_tokens, width, ld_res, block,
+                        kept_blocks, n_kept, y, ld_y, y_rows, dev_status, stream, true);
 }
 
 size_t lemo_mlp_block_scores_workspace(int n_tokens, int width, int block) {
@@ -358,14 +378,15 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
           n_tokens, block, d_in, d_out, cap_rows, pad_multiple);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
+  REQUIRE((cap_rows + 255LL) / 256 * ((d_out + 255) / 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "cap_rows %d x d_out %d: more than %lld tiles of 256 x 256 for one launch", cap_rows, d_out,
+          kMaxFusedWorkgroups);
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_in, "x")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
   if ((st = check_rows(y, ld_y, d_out, "y")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
-  REQUIRE((cap_rows + 127LL) / 128 * ((d_out + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
-          "cap_rows %d x d_out %d: too many tiles for one launch", cap_rows, d_out);
   return device_status(lemo_launch_gather_linear(x, n_tokens, d_in, ld_x, block, kept_blocks, n_kept, weight, d_out,
                                                  ld_w, y, ld_y, cap_rows, pad_multiple, dev_status,
                                                  static_cast<hipStream_t>(stream)),
@@ -382,14 +403,17 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
           cap_rows);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
+  // the product covers min(cap_rows, n_tokens) rows (no more rows can be kept)
+  const long long prod_rows = cap_rows < n_tokens ? cap_rows : n_tokens;
+  REQUIRE((prod_rows + 255) / 256 * ((d_out + 255) / 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
+          "%lld rows x d_out %d: more than %lld tiles of 256 x 256 for one launch", prod_rows, d_out,
+          kMaxFusedWorkgroups);
   lemo_status st;
   if ((st = check_rows(a, ld_a, d_in, "a")) != LEMO_OK) return st;
   if ((st = check_rows(weight, ld_w, d_in, "weight")) != LEMO_OK) return st;
   if ((st = check_rows(residual, ld_res, d_out, "residual")) != LEMO_OK) return st;
   if ((st = check_offsets(cap_rows, ld_a, "a")) != LEMO_OK) return st;
   if ((st = check_offsets(d_out, ld_w, "weight")) != LEMO_OK) return st;
-  REQUIRE((cap_rows + 127LL) / 128 * ((d_out + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
-          "cap_rows %d x d_out %d: too many tiles for one launch", cap_rows, d_out);
   return device_status(lemo_launch_linear_scatter(a, d_in, ld_a, cap_rows, weight, d_out, ld_w, residual, n_tokens,
                                                   ld_res, block, kept_blocks, n_kept, dev_status,
                                                   static_cast<hipStream_t>(stream)),

@@ -74,10 +74,11 @@ hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int 
                               const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst,
                               int cap_rows, int pad_multiple, int32_t* dev_status, hipStream_t stream);
 
-// subtract: the backward recompute res -= y instead of res += y
+// subtract: the backward recompute res -= y instead of res += y.  y holds
+// y_rows rows (kept rows past them are skipped and flag a capacity overflow).
 hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block,
                                const int32_t* kept, const int32_t* n_kept, const uint16_t* y, int ld_y,
-                               int32_t* dev_status, hipStream_t stream, bool subtract = false);
+                               int y_rows, int32_t* dev_status, hipStream_t stream, bool subtract = false);
 
 // MLP-block scores: act [n_tokens][ld_act]; with `up` non-NULL, act is the
 // gate projection and the activation is SiLU(act) * up.  Workspace: fp32

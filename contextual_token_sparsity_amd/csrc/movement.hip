@@ -117,18 +117,25 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
 }
 
 // res[token(p)] = res[token(p)] + y[p] for the kept rows p (SUB: minus).
+// y holds y_rows rows: kept rows at or past y_rows are left out (their
+// residual rows stay untouched) and flag LEMO_DEV_CAP_OVERFLOW.
 template <bool SUB>
 __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res, int n_tokens, int width, int ld_res,
                                                       int block, const int32_t* __restrict__ kept,
                                                       const int32_t* __restrict__ n_kept_p,
-                                                      const uint16_t* __restrict__ y, int ld_y,
+                                                      const uint16_t* __restrict__ y, int ld_y, int y_rows,
                                                       int32_t* __restrict__ status) {
   const int nb = (n_tokens + block - 1) / block;
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
-  const int n_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
-  if (status && bad_count && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
-    atomicOr(status, LEMO_DEV_BAD_KEPT);
+  const int all_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
+  const int n_rows = min(all_rows, y_rows);
+  if (status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    int flags = 0;
+    if (bad_count) flags |= LEMO_DEV_BAD_KEPT;
+    if (all_rows > y_rows) flags |= LEMO_DEV_CAP_OVERFLOW;
+    if (flags) atomicOr(status, flags);
+  }
   const int ch = blockIdx.x * kThreads + threadIdx.x;
   if (ch * 8 >= width) return;
   const int step = gridDim.y;
@@ -180,13 +187,14 @@ hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int 
 }
 
 hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block, const int32_t* kept,
-                               const int32_t* n_kept, const uint16_t* y, int ld_y, int32_t* dev_status,
+                               const int32_t* n_kept, const uint16_t* y, int ld_y, int y_rows, int32_t* dev_status,
                                hipStream_t stream, bool subtract) {
+  const dim3 grid = grid_for(width, min(n_tokens, y_rows));
   if (subtract)
-    hipLaunchKernelGGL(k_scatter<true>, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens,
-                       width, ld_res, block, kept, n_kept, y, ld_y, dev_status);
+    hipLaunchKernelGGL(k_scatter<true>, grid, dim3(kThreads), 0, stream, res, n_tokens, width, ld_res, block, kept,
+                       n_kept, y, ld_y, y_rows, dev_status);
   else
-    hipLaunchKernelGGL(k_scatter<false>, grid_for(width, n_tokens), dim3(kThreads), 0, stream, res, n_tokens,
-                       width, ld_res, block, kept, n_kept, y, ld_y, dev_status);
+    hipLaunchKernelGGL(k_scatter<false>, grid, dim3(kThreads), 0, stream, res, n_tokens, width, ld_res, block, kept,
+                       n_kept, y, ld_y, y_rows, dev_status);
   return hipGetLastError();
 }

@@ -38,6 +38,8 @@ _SIGS = {
     "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "lemo_residual_recompute": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_scatter_residual_capped": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
+    "lemo_residual_recompute_capped": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "lemo_mlp_block_scores_workspace": (_sz, [_i, _i, _i]),
     "lemo_mlp_block_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "lemo_mlp_block_scores_gated": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -317,34 +319,50 @@ def lemo_gather_pad(src, block: int, kept_blocks, n_kept, dst, pad_multiple: int
     return dst
 
 
-def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: int = None, n_tokens: int = None,
-                          dev_status=None):
-    """In-place addition of y's rows into the kept rows of residual."""
+def _scatter(fn, residual, block, kept_blocks, n_kept, y, width, n_tokens, dev_status, y_rows):
     _bf16(residual), _bf16(y)
     w = residual.shape[1] if width is None else width
     n = residual.shape[0] if n_tokens is None else n_tokens
+    rows = y.shape[0] if y_rows is None else y_rows
     _rows_within(residual, n, w, "residual")
-    _rows_within(y, 0, w, "y")
+    _rows_within(y, rows, w, "y")
     _kept_bufs(kept_blocks, n_kept, dev_status, residual.device)
-    st = lib().lemo_scatter_residual(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
-                                     _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
-    _check(st, "lemo_scatter_residual")
+    st = getattr(lib(), fn)(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept), _ptr(y),
+                            _ld(y), rows, _ptr(dev_status), _stream(residual.device))
+    _check(st, fn)
     return residual
+
+
+def lemo_scatter_residual(residual, block: int, kept_blocks, n_kept, y, width: int = None, n_tokens: int = None,
+                          dev_status=None):
+    """In-place addition of y's rows into the kept rows of residual.  Calls
+    the capped entry point with y's row count, so a layer output shorter than
+    the kept rows is never read past its end (the rows it lacks are left out
+    and flag DEV_CAP_OVERFLOW)."""
+    return _scatter("lemo_scatter_residual_capped", residual, block, kept_blocks, n_kept, y, width, n_tokens,
+                    dev_status, None)
+
+
+def lemo_scatter_residual_capped(residual, block: int, kept_blocks, n_kept, y, y_rows: int = None,
+                                 width: int = None, n_tokens: int = None, dev_status=None):
+    """lemo_scatter_residual with an explicit count of y's rows (default: all of them)."""
+    return _scatter("lemo_scatter_residual_capped", residual, block, kept_blocks, n_kept, y, width, n_tokens,
+                    dev_status, y_rows)
 
 
 def lemo_residual_recompute(residual, block: int, kept_blocks, n_kept, y, width: int = None, n_tokens: int = None,
                             dev_status=None):
-    """Backward recompute: subtracts y's rows from the kept rows of residual, in place."""
-    _bf16(residual), _bf16(y)
-    w = residual.shape[1] if width is None else width
-    n = residual.shape[0] if n_tokens is None else n_tokens
-    _rows_within(residual, n, w, "residual")
-    _rows_within(y, 0, w, "y")
-    _kept_bufs(kept_blocks, n_kept, dev_status, residual.device)
-    st = lib().lemo_residual_recompute(_ptr(residual), n, w, _ld(residual), block, _ptr(kept_blocks), _ptr(n_kept),
-                                       _ptr(y), _ld(y), _ptr(dev_status), _stream(residual.device))
-    _check(st, "lemo_residual_recompute")
-    return residual
+    """Backward recompute: subtracts y's rows from the kept rows of residual,
+    in place (capped at y's row count as lemo_scatter_residual is)."""
+    return _scatter("lemo_residual_recompute_capped", residual, block, kept_blocks, n_kept, y, width, n_tokens,
+                    dev_status, None)
+
+
+def lemo_residual_recompute_capped(residual, block: int, kept_blocks, n_kept, y, y_rows: int = None,
+                                   width: int = None, n_tokens: int = None, dev_status=None):
+    """lemo_residual_recompute with an explicit count of y's rows (default: all of them)."""
+    return _scatter("lemo_residual_recompute_capped", residual, block, kept_blocks, n_kept, y, width, n_tokens,
+                    dev_status, y_rows)
 
 
 def lemo_mlp_block_scores_workspace(n_tokens: int, width: int, block: int) -> int:

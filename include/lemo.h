@@ -286,9 +286,12 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
  *   bf16(a[p] weight^T)) for p < R, in place; other rows untouched.  a holds
  *   the kept rows densely, [cap_rows][ld_a] (d_in used); kept rows past
  *   cap_rows are skipped and flag LEMO_DEV_CAP_OVERFLOW.
- * Invalid kept indices are skipped and flag LEMO_DEV_BAD_KEPT.
- * d_in a multiple of 64, d_out a multiple of 8.  Errors: INVALID_ARG,
- * UNSUPPORTED (d_in), ALIGNMENT (pointers, ld, d_out).
+ * Invalid kept indices are skipped and flag LEMO_DEV_BAD_KEPT; kept_blocks
+ * must hold distinct indices (see lemo_scatter_residual).
+ * d_in a multiple of 64, d_out a multiple of 8.  One launch holds at most
+ * (2^31 - 1) / 512 output tiles of 256 x 256 (rows: cap_rows for the gather,
+ * min(cap_rows, n_tokens) for the scatter).  Errors: INVALID_ARG,
+ * UNSUPPORTED (d_in, tile count), ALIGNMENT (pointers, ld, d_out).
  * ------------------------------------------------------------------------ */
 lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int ld_x, int block,
                                const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* weight,
@@ -310,11 +313,29 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
  *  ragged sequence's short last block).
  *  (fp32 add then round-to-nearest-even: the correctly rounded bf16 sum.)
  *  y             bf16 [>= n_kept*block][ld_y], rows in kept order (as
- *                lemo_gather_pad lays them out).
+ *                lemo_gather_pad lays them out).  lemo_scatter_residual
+ *                trusts the caller on this: y must hold every kept row.
+ *  kept_blocks   distinct block indices (lemo_select_mask's ascending list
+ *                is); a block listed twice makes two unsynchronised updates
+ *                of the same residual rows, whose result is unspecified.
+ *                The same holds for lemo_residual_recompute and
+ *                lemo_linear_scatter.
+ *
+ * lemo_scatter_residual_capped: the same with the number of rows y holds,
+ *  y_rows >= 0, as an argument.  Kept rows p >= y_rows (possible when the
+ *  layer output was built from a gather that hit its capacity) are left out:
+ *  their residual rows stay untouched, y is never read past row y_rows - 1,
+ *  and LEMO_DEV_CAP_OVERFLOW is set in dev_status.
+ * Invalid kept indices are skipped and flag LEMO_DEV_BAD_KEPT.  width a
+ * multiple of 8; ld_res, ld_y >= width, multiples of 8.  Errors: INVALID_ARG
+ * (NULL, sizes, negative y_rows, ld < width), ALIGNMENT (pointers, ld, width).
  * ------------------------------------------------------------------------ */
 lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
                                   const int32_t* kept_blocks, const int32_t* n_kept,
                                   const lemo_bf16* y, int ld_y, int32_t* dev_status, void* stream);
+lemo_status lemo_scatter_residual_capped(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                         const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y,
+                                         int ld_y, int y_rows, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward recompute of a layer's input (Jenga 4.2.3, in-place addition:
@@ -327,11 +348,16 @@ lemo_status lemo_scatter_residual(lemo_bf16* residual, int n_tokens, int width, 
  *  addition never changed, are left bit-identical.  When the forward
  *  addition rounded, the result is not the input bit for bit: each element
  *  is within half a bf16 spacing at the output value plus half a spacing at
- *  the result.  Arguments, errors and dev_status as lemo_scatter_residual.
+ *  the result.  Arguments, errors and dev_status as lemo_scatter_residual;
+ *  lemo_residual_recompute_capped takes y_rows as
+ *  lemo_scatter_residual_capped does.
  * ------------------------------------------------------------------------ */
 lemo_status lemo_residual_recompute(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
                                    const int32_t* kept_blocks, const int32_t* n_kept,
                                    const lemo_bf16* y, int ld_y, int32_t* dev_status, void* stream);
+lemo_status lemo_residual_recompute_capped(lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,
+                                          const int32_t* kept_blocks, const int32_t* n_kept, const lemo_bf16* y,
+                                          int ld_y, int y_rows, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------
  * Token-block scores from the MLP block (Jenga 4.2.1, "Extend to MLP

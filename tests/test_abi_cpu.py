@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
 
@@ -216,6 +216,46 @@ def rc(L, res=P, n=1024, w=64, ldr=64, b=64, kept=P, nk=P, y=P, ldy=64):
 def test_residual_recompute_rejects(L, kw, status):
     assert rc(L, **kw) == status
     assert lemo.lemo_last_error()
+
+
+def scc(L, res=P, n=1024, w=512, ldr=512, b=64, kept=P, nk=P, y=P, ldy=512, rows=64, recompute=False):
+    fn = L.lemo_residual_recompute_capped if recompute else L.lemo_scatter_residual_capped
+    return fn(res, n, w, ldr, b, kept, nk, y, ldy, rows, NULL, NULL)
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(kept=NULL), INVALID), (dict(nk=NULL), INVALID), (dict(res=NULL), INVALID), (dict(y=NULL), INVALID),
+    (dict(rows=-1), INVALID), (dict(b=0), INVALID), (dict(ldy=256), INVALID),
+    (dict(w=4, ldr=8, ldy=8), ALIGN), (dict(y=P2), ALIGN), (dict(res=P2), ALIGN),
+])
+def test_scatter_capped_rejects(L, kw, status, recompute):
+    """The capped scatter and recompute (y's row count as an argument) check
+    what the plain calls check, and refuse a negative row count."""
+    assert scc(L, recompute=recompute, **kw) == status
+    assert lemo.lemo_last_error()
+    if kw == dict(rows=-1):
+        assert "y_rows" in lemo.lemo_last_error()
+
+
+def test_fused_tile_limit(L):
+    """The fused products launch one 512-thread workgroup per 256 x 256 output
+    tile, at most (2^31 - 1) / 512 of them.  Just past that is refused; just
+    inside it passes the tile check (and these calls stop at the NULL output
+    checked next), although the old 128 x 128 count refused it."""
+    lim = ((1 << 31) - 1) // 512
+    assert lim == 4194303
+    ok_cap, bad_cap = lim * 256, (lim + 1) * 256
+    assert L.lemo_gather_linear(P, 1024, 64, 64, 64, P, P, P, 256, 64, P, 256, bad_cap, 1, NULL, NULL) == UNSUP
+    assert "256 x 256" in lemo.lemo_last_error()
+    assert L.lemo_gather_linear(P, 1024, 64, 64, 64, P, P, P, 256, 64, NULL, 256, ok_cap, 1, NULL, NULL) == INVALID
+    assert "y is NULL" in lemo.lemo_last_error()
+    # the scatter's product covers min(cap_rows, n_tokens) rows
+    rows = (1 << 25) - 1                      # ceil(rows / 256) = 131072 row tiles
+    assert L.lemo_linear_scatter(P, 64, 64, rows, P, 8192, 64, P, rows, 8192, 64, P, P, NULL, NULL) == UNSUP
+    assert L.lemo_linear_scatter(P, 64, 64, rows, P, 7936, 64, NULL, rows, 8192, 64, P, P, NULL, NULL) == INVALID
+    assert "residual is NULL" in lemo.lemo_last_error()
+    assert L.lemo_linear_scatter(P, 64, 64, rows, P, 8192, 64, NULL, 1024, 8192, 64, P, P, NULL, NULL) == INVALID
 
 
 def test_mlp_workspace_query(L):

@@ -799,6 +799,46 @@ def test_bad_kept_indices_are_skipped_and_flagged():
     assert np.array_equal(host_bits(resd), res) and int(status.item()) & lemo.DEV_BAD_KEPT
 
 
+@pytest.mark.parametrize("recompute", [False, True], ids=["scatter", "recompute"])
+def test_scatter_capped_short_layer_output(recompute):
+    """A layer output with fewer rows than the kept rows (built from a gather
+    that hit its capacity): the binding passes y's row count, the kept rows
+    past it are left out (their residual rows untouched, y never read past its
+    end) and the capacity flag is set; an explicit smaller count and a count
+    of 0 behave the same way."""
+    n, w, b = 512, 64, 16
+    rng = np.random.default_rng(21 + recompute)
+    kept = np.arange(0, 32, 2, dtype=np.int32)          # 16 blocks = 256 kept rows
+    nk = kept.size
+    rows = O.kept_token_rows(kept, nk, b)
+    res = synth.random_bf16(rng, (n, w))
+    kd, nkd = dev(kept), dev(np.array([nk], np.int32))
+    oracle = O.residual_recompute if recompute else O.scatter_residual
+    call = lemo.lemo_residual_recompute if recompute else lemo.lemo_scatter_residual
+    call_capped = lemo.lemo_residual_recompute_capped if recompute else lemo.lemo_scatter_residual_capped
+    y_short = synth.random_bf16(rng, (200, w))
+    for y_rows, use_capped in ((200, False), (120, True), (0, True)):
+        say("scatter capped", recompute, y_rows)
+        y_ext = np.zeros((rows.size, w), np.uint16)
+        y_ext[:y_rows] = y_short[:y_rows]
+        ref = oracle(res, b, kept, nk, y_ext)
+        ref[rows[y_rows:]] = res[rows[y_rows:]]           # rows past the layer output: untouched
+        resd = dev(res)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if use_capped:
+            call_capped(resd, b, kd, nkd, dev(y_short), y_rows=y_rows, dev_status=status)
+        else:
+            call(resd, b, kd, nkd, dev(y_short), dev_status=status)
+        assert np.array_equal(host_bits(resd), ref)
+        assert int(status.item()) == lemo.DEV_CAP_OVERFLOW
+    # enough rows: no flag, same as the plain call
+    y_full = synth.random_bf16(rng, (rows.size, w))
+    resd = dev(res)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    call_capped(resd, b, kd, nkd, dev(y_full), dev_status=status)
+    assert np.array_equal(host_bits(resd), oracle(res, b, kept, nk, y_full)) and int(status.item()) == 0
+
+
 def test_movement_full_size_oracle_mask():
     """The benchmark's Llama2-7B N=16K movement with the oracle's predicted
     mask (MEAN threshold): gather of X and of the MLP activation padded to
