@@ -9,11 +9,12 @@
 //                 count: block, or fewer for the last block of a ragged sequence)
 //                 -- one pass over X, the only HBM-heavy phase.
 //   k_hidden      part[s][m][n] = xbar[m, Ks] . [U_q | U_k][Ks, n]  (bf16 MFMA,
-//                 split over s = slices Ks of d_model so that ~1000 waves run)
+//                 split over slices Ks of d_model so that ~512 workgroups run;
+//                 U transposed through LDS)
 //   k_project     hid = bf16(max(0, sum_s part[s])) (fixed slice order), then
-//                 q_hat = hid_q V_q, k_hat = hid_k V_k in fp32
-//   k_pair        M_hat[m][n] = max(0, q_hat[m] . k_hat[n])  (fp32, 16 x 16 tiles)
-//   k_colsum      I_hat[n] = sum_m M_hat[m][n]
+//                 q_hat = hid_q V_q (stored transposed), k_hat = hid_k V_k in fp32
+//   k_pair_colsum I_hat[n] = sum_m max(0, q_hat[m] . k_hat[n]) in a fixed
+//                 order; M_hat is written only when the caller asks for it.
 #include "lemo_internal.h"
 
 namespace {
@@ -60,106 +61,209 @@ __global__ __launch_bounds__(64) void k_pool(const uint16_t* __restrict__ X, int
 }
 
 // ------------------------------------------------------- hidden (split-K)
-// Each wave computes one 32 x 32 tile (rows = blocks, cols = predictor
-// neurons; cols < rank from U_q, the rest from U_k) over one slice of the
-// model dimension with v_mfma_f32_32x32x16_bf16.  The B operand (a column
-// of U) is strided in memory: each lane gathers its 8 k-values with 2-byte
-// loads, coalesced across the 32 lanes that share a k.
+// part[s][m][n] = xbar[m, Ks] . [U_q | U_k][Ks, n] for the 32 x 32 tile
+// (rows m = blocks, columns n = predictor neurons; n < rank from U_q, the
+// rest from U_k) of a workgroup and its slice Ks of the model dimension.
+// The slice is split over the 4 waves (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation) and walked in chunks of 64; the waves' sums are added in
+// wave order through LDS.  The MFMA B operand needs 8 consecutive k of one
+// neuron per lane, but U is stored [d][rank] (neurons contiguous): each
+// lane loads two adjacent U rows (16 bytes of 8 neurons each) and writes
+// the (k, k+1) pairs of each neuron as one 4-byte word into its wave's LDS
+// tile, stored neuron-major, from which the operand is one 16-byte read.
+// (Measured: this beats 2-byte gathers of U columns, the 2-byte transposed
+// stores, and issuing a whole 128-k round of loads at once.)
+constexpr int kHidChunk = 64;                    // k per LDS round
+constexpr int kHidLd = kHidChunk + 8;            // LDS row stride (elements): 144 B
+
 __global__ __launch_bounds__(256) void k_hidden(const uint16_t* __restrict__ xbar, int d, int nb,
                                                 const uint16_t* __restrict__ uq, const uint16_t* __restrict__ uk,
-                                                int rank, int kslice, int n_mt, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63;
-  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n_nt = (2 * rank) / 32;
-  if (tile >= n_mt * n_nt) return;
-  const int mt = tile / n_nt, nt = tile % n_nt;
+                                                int rank, int kslice, int n_nt, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t ut[4][32][kHidLd];
+  __shared__ float red[3][64][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int mt = blockIdx.x / n_nt, nt = blockIdx.x % n_nt;
   const int s = blockIdx.y;
   const int m0 = mt * 32, n0 = nt * 32;
   const uint16_t* U = n0 < rank ? uq : uk;
-  const int nn = (n0 % rank) + (lane & 31);
-  const int row = m0 + (lane & 31);
-  const bool row_ok = row < nb;
-  const int kbeg = s * kslice;
+  const int u0 = n0 % rank;                      // first neuron of the tile within U
+  const int row = min(m0 + l32, nb - 1);         // rows past nb read a valid row; dropped below
+  const int kw = kslice / 4;                     // this wave's share, a multiple of 16
+  const int kbeg = s * kslice + wave * kw;
+  const uint16_t* arow = xbar + (size_t)row * d + 8 * hi;
   lemo_f32x16 acc = {};
-  for (int k = kbeg; k < kbeg + kslice; k += 16) {
-    const int kk = k + 8 * (lane >> 5);
-    lemo_i16x8 a = {};
-    if (row_ok) a = *reinterpret_cast<const lemo_i16x8*>(xbar + (size_t)row * d + kk);
-    lemo_i16x8 b;
+  for (int c0 = 0; c0 < kw; c0 += kHidChunk) {
+    const int cl = min(kHidChunk, kw - c0);      // a multiple of 16
+    lemo_bf16x8 a[kHidChunk / 16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = (short)U[(size_t)(kk + j) * rank + nn];
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(lemo_bf16x8, a),
-                                                  __builtin_bit_cast(lemo_bf16x8, b), acc, 0, 0, 0);
+    for (int i = 0; i < kHidChunk / 16; ++i)
+      if (16 * i < cl) a[i] = *reinterpret_cast<const lemo_bf16x8*>(arow + kbeg + c0 + 16 * i);
+    // pair P = i * 64 + lane: U rows r = 2 (P / 4) and r + 1 of the chunk,
+    // neurons u0 + 8 (P % 4) .. + 7
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int P = i * 64 + lane, r = 2 * (P >> 2), pc = P & 3;
+      if (r < cl) {
+        const uint16_t* up = U + (size_t)(kbeg + c0 + r) * rank + u0 + pc * 8;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(up);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(up + rank);
+        const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
+        const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<uint32_t*>(&ut[wave][pc * 8 + 2 * j][r]) = (w0[j] & 0xffffu) | (w1[j] << 16);
+          *reinterpret_cast<uint32_t*>(&ut[wave][pc * 8 + 2 * j + 1][r]) = (w0[j] >> 16) | (w1[j] & 0xffff0000u);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kHidChunk / 16; ++i) {
+      if (16 * i < cl) {
+        const lemo_bf16x8 b = *reinterpret_cast<const lemo_bf16x8*>(&ut[wave][l32][16 * i + 8 * hi]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // operand reads done before the tile is rewritten
+    __builtin_amdgcn_wave_barrier();
   }
-  float* out = part + (size_t)s * nb * (2 * rank);
+  // the four waves' partial tiles, added in wave order
+  if (wave > 0) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int r = m0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-    if (r < nb) out[(size_t)r * (2 * rank) + n0 + (lane & 31)] = acc[e];
+    for (int e = 0; e < 16; ++e) red[wave - 1][lane][e] = acc[e];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += red[w][lane][e];
+    float* out = part + (size_t)s * nb * (2 * rank);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = m0 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (r < nb) out[(size_t)r * (2 * rank) + n0 + l32] = acc[e];
+    }
   }
 }
 
 // ------------------------------------------------------------- projection
-// One workgroup per block row m, 2*rank threads: thread t first forms hidden
-// unit t (slices summed in order, ReLU, bf16), then output t of q_hat
-// (t < rank) or k_hat (t >= rank) as a sequential fp32 dot over the rank.
+// One block m per workgroup, 2*rank threads: thread t forms hidden unit t
+// (the slices' partial sums, all loaded at once, added in slice order;
+// ReLU; bf16), then output t of q_hat (t < rank) or k_hat (t >= rank) as a
+// sequential fp32 dot over the rank, reading V's column t in rounds of 32
+// loads.  q_hat is stored transposed, [rank][nb], so that the pair kernel's
+// threads (one per query block) read it with coalesced loads.
+constexpr int kProjMaxSlices = 16;
+
 __global__ __launch_bounds__(512) void k_project(const float* __restrict__ part, int nslices, int nb, int rank,
                                                  const uint16_t* __restrict__ vq, const uint16_t* __restrict__ vk,
-                                                 float* __restrict__ qhat, float* __restrict__ khat) {
+                                                 float* __restrict__ qhat_t, float* __restrict__ khat) {
   __shared__ float hid[512];
   const int m = blockIdx.x, t = threadIdx.x;
   const int width = 2 * rank;
+  float pv[kProjMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kProjMaxSlices; ++s)
+    if (s < nslices) pv[s] = part[((size_t)s * nb + m) * width + t];
   float h = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < nslices; ++s) h += part[((size_t)s * nb + m) * width + t];
-  h = fmaxf(h, 0.f);
-  hid[t] = lemo_bf16_to_f32(lemo_f32_to_bf16(h));
+#pragma unroll
+  for (int s = 0; s < kProjMaxSlices; ++s)
+    if (s < nslices) h += pv[s];
+  hid[t] = lemo_bf16_to_f32(lemo_f32_to_bf16(fmaxf(h, 0.f)));
   __syncthreads();
   const bool is_q = t < rank;
   const int v = is_q ? t : t - rank;
   const uint16_t* V = is_q ? vq : vk;
   const float* hh = hid + (is_q ? 0 : rank);
-  // the V column is read 16 rows at a time so its loads overlap; the sum
-  // still runs over u in order
   float acc = 0.f;
-  for (int u0 = 0; u0 < rank; u0 += 16) {
-    float vv[16];
+  for (int u0 = 0; u0 < rank; u0 += 32) {
+    float vv[32];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) vv[j] = lemo_bf16_to_f32(V[(size_t)(u0 + j) * rank + v]);
+    for (int j = 0; j < 32; ++j) vv[j] = lemo_bf16_to_f32(V[(size_t)(u0 + j) * rank + v]);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc = fmaf(hh[u0 + j], vv[j], acc);
+    for (int j = 0; j < 32; ++j) acc = fmaf(hh[u0 + j], vv[j], acc);
   }
-  (is_q ? qhat : khat)[(size_t)m * rank + v] = acc;
+  if (is_q)
+    qhat_t[(size_t)v * nb + m] = acc;
+  else
+    khat[(size_t)m * rank + v] = acc;
 }
 
-// ------------------------------------------------------------ pair scores
-// 16 x 16 tile of M_hat per workgroup, one output per thread; q_hat / k_hat
-// rows staged in LDS in 64-wide slices of the rank; the dot runs over v in
-// order.
-__global__ __launch_bounds__(256) void k_pair(const float* __restrict__ qhat, const float* __restrict__ khat,
-                                              int nb, int rank, float* __restrict__ M) {
-  __shared__ float sq[16][65];
-  __shared__ float sk[16][65];
-  const int n0 = blockIdx.x * 16, m0 = blockIdx.y * 16;
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  float acc = 0.f;
-  for (int v0 = 0; v0 < rank; v0 += 64) {
-    for (int i = t; i < 16 * 64; i += 256) {
-      const int r = i >> 6, c = i & 63;
-      const bool in = v0 + c < rank;   // rank is a multiple of 32, the slice is 64 wide
-      sq[r][c] = (m0 + r < nb && in) ? qhat[(size_t)(m0 + r) * rank + v0 + c] : 0.f;
-      sk[r][c] = (n0 + r < nb && in) ? khat[(size_t)(n0 + r) * rank + v0 + c] : 0.f;
+// ------------------------------------------- pair scores and column sums
+// A workgroup owns NC key blocks n; thread t walks the query blocks
+// m = t, t + 256, ...: M_hat[m][n] = max(0, q_hat[m] . k_hat[n]) (fp32 dot
+// in v order; q_hat read column-wise from its transposed copy, 64 values at
+// a time with every load of the round issued before the k_hat rows are
+// staged in LDS), written only when the caller asked for the block matrix,
+// and summed per thread in m order; the per-thread sums are then added in
+// a fixed order (a butterfly inside each wave, then the four waves in
+// order), so I_hat[n] is deterministic.
+template <int NC>
+__global__ __launch_bounds__(256) void k_pair_colsum(const float* __restrict__ qhat_t, const float* __restrict__ khat,
+                                                     int nb, int rank, float* __restrict__ M,
+                                                     float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) float kt[NC][256];
+  __shared__ float red[NC][4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n0 = blockIdx.x * NC;
+  float cs[NC] = {};
+  bool staged = false;
+  for (int m0 = 0; m0 < nb; m0 += 256) {
+    const int m = m0 + t;
+    const float* qc = qhat_t + min(m, nb - 1);
+    float dot[NC] = {};
+    for (int v0 = 0; v0 < rank; v0 += 64) {
+      float q[64];
+#pragma unroll
+      for (int j = 0; j < 64; ++j)
+        if (v0 + j < rank) q[j] = qc[(size_t)(v0 + j) * nb];
+      if (!staged) {   // uniform: every thread reaches it in the same round
+        for (int i = t; i < NC * rank; i += 256) {
+          const int n = i / rank, v = i % rank;
+          kt[n][v] = n0 + n < nb ? khat[(size_t)(n0 + n) * rank + v] : 0.f;
+        }
+        __syncthreads();
+        staged = true;
+      }
+#pragma unroll
+      for (int j = 0; j < 64; j += 4) {
+        if (v0 + j < rank) {   // rank is a multiple of 32
+#pragma unroll
+          for (int n = 0; n < NC; ++n) {
+            const float4 k4 = *reinterpret_cast<const float4*>(&kt[n][v0 + j]);
+            dot[n] = fmaf(q[j], k4.x, dot[n]);
+            dot[n] = fmaf(q[j + 1], k4.y, dot[n]);
+            dot[n] = fmaf(q[j + 2], k4.z, dot[n]);
+            dot[n] = fmaf(q[j + 3], k4.w, dot[n]);
+          }
+        }
+      }
     }
-    __syncthreads();
-#pragma unroll 16
-    for (int v = 0; v < 64; ++v) acc = fmaf(sq[ty][v], sk[tx][v], acc);
-    __syncthreads();
+    if (m < nb) {
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        const float val = fmaxf(dot[n], 0.f);
+        cs[n] += val;
+        if (M && n0 + n < nb) M[(size_t)m * nb + n0 + n] = val;
+      }
+    }
   }
-  if (m0 + ty < nb && n0 + tx < nb) M[(size_t)(m0 + ty) * nb + n0 + tx] = fmaxf(acc, 0.f);
+#pragma unroll
+  for (int n = 0; n < NC; ++n) {
+    float v = cs[n];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) red[n][wave] = v;
+  }
+  __syncthreads();
+  if (t < NC && n0 + t < nb) scores[n0 + t] = ((red[t][0] + red[t][1]) + red[t][2]) + red[t][3];
 }
 
 struct Layout {
-  size_t xbar, part, qhat, khat, m, total;
+  size_t xbar, part, qhat, khat, total;   // qhat: transposed, [rank][nb]
 };
 
 Layout layout(int n_tokens, int d_model, int block, int rank) {
@@ -171,20 +275,24 @@ Layout layout(int n_tokens, int d_model, int block, int rank) {
   L.part = off; off += lemo_align256((size_t)s * nb * 2 * rank * 4);
   L.qhat = off; off += lemo_align256((size_t)nb * rank * 4);
   L.khat = off; off += lemo_align256((size_t)nb * rank * 4);
-  L.m = off;    off += lemo_align256((size_t)nb * nb * 4);
   L.total = off;
   return L;
 }
 
 }  // namespace
 
-// Number of d_model slices for the hidden product: enough 32 x 32 tiles x
-// slices to give about 1024 waves, each slice a multiple of 16 columns.
+// Number of d_model slices for the hidden product: each workgroup takes one
+// slice of d_model (split over its 4 waves in multiples of 16).  Enough
+// slices to give about 512 workgroups, at most 16 (the projection adds
+// them), each at least 256 columns wide (64 per wave) and dividing d_model
+// into multiples of 64 columns.
 int lemo_predict_splitk(int nb, int d_model, int rank) {
   const int tiles = ((nb + 31) / 32) * ((2 * rank) / 32);
-  int s = 1;
-  while (s * tiles < 1024 && (d_model % (32 * s)) == 0 && d_model / (2 * s) >= 64) s *= 2;
-  return s;
+  const int want = (512 + tiles - 1) / tiles;
+  int best = 1;
+  for (int s = 2; s <= 16 && s <= want; ++s)
+    if ((d_model / 64) % s == 0 && d_model / s >= 256) best = s;
+  return best;
 }
 
 size_t lemo_predict_ws_bytes(int n_tokens, int d_model, int block, int rank) {
@@ -202,17 +310,18 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
   float* part = reinterpret_cast<float*>(ws + L.part);
   float* qhat = reinterpret_cast<float*>(ws + L.qhat);
   float* khat = reinterpret_cast<float*>(ws + L.khat);
-  float* M = m_out ? m_out : reinterpret_cast<float*>(ws + L.m);
 
   hipLaunchKernelGGL(k_pool, dim3((d_model / 8 + 63) / 64, nb), dim3(64), 0, st, x, ld_x, d_model, block, n_tokens,
                      1.0f / (float)block, xbar);
   const int s = lemo_predict_splitk(nb, d_model, rank);
   const int n_mt = (nb + 31) / 32, n_nt = (2 * rank) / 32;
-  hipLaunchKernelGGL(k_hidden, dim3((n_mt * n_nt + 3) / 4, s), dim3(256), 0, st, xbar, d_model, nb, u_q, u_k,
-                     rank, d_model / s, n_mt, part);
+  hipLaunchKernelGGL(k_hidden, dim3(n_mt * n_nt, s), dim3(256), 0, st, xbar, d_model, nb, u_q, u_k, rank,
+                     d_model / s, n_nt, part);
   hipLaunchKernelGGL(k_project, dim3(nb), dim3(2 * rank), 0, st, part, s, nb, rank, v_q, v_k, qhat, khat);
-  hipLaunchKernelGGL(k_pair, dim3((nb + 15) / 16, (nb + 15) / 16), dim3(256), 0, st, qhat, khat, nb, rank, M);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return lemo_launch_colsum(M, nb, scores, st);
+  // one key block per workgroup while that still gives few workgroups
+  if (nb <= 1024)
+    hipLaunchKernelGGL(k_pair_colsum<1>, dim3(nb), dim3(256), 0, st, qhat, khat, nb, rank, m_out, scores);
+  else
+    hipLaunchKernelGGL(k_pair_colsum<2>, dim3((nb + 1) / 2), dim3(256), 0, st, qhat, khat, nb, rank, m_out, scores);
+  return hipGetLastError();
 }

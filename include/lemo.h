@@ -183,9 +183,12 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
  *  block         power of two, 2..256; nb = ceil(n_tokens / block) <= 65535.
  *  d_model       multiple of 64.   rank: multiple of 32, at most 256.
  *  u_q, u_k      bf16 [d_model][rank] row-major.  v_q, v_k: bf16 [rank][rank].
- *  block_scores  optional fp32 [nb][nb] M_hat (NULL: kept in workspace).
+ *  block_scores  optional fp32 [nb][nb] M_hat (NULL: M_hat is never stored;
+ *                the column aggregate is formed on the fly).
  *  scores        fp32 [nb] I_hat.
- *  workspace     lemo_predict_scores_workspace() bytes.
+ *  workspace     lemo_predict_scores_workspace() bytes, 16-byte aligned:
+ *                xbar, split-K partial sums of the hidden layer, q_hat, k_hat
+ *                (it does not grow with nb^2).
  * Errors: INVALID_ARG, UNSUPPORTED (block, d_model, rank), ALIGNMENT, WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int rank);

@@ -36,8 +36,9 @@ def test_workspace_queries(L):
     assert L.lemo_block_scores_workspace(16384, 64) == 256 * 256 * 4
     assert L.lemo_block_scores_workspace(100, 64) == 0
     ws = L.lemo_predict_scores_workspace(16384, 4096, 64, 128)
-    # xbar (2 MiB) + split-K partials + q_hat/k_hat + M_hat
-    assert ws >= 256 * 4096 * 2 + 2 * 256 * 128 * 4 + 256 * 256 * 4
+    # xbar (2 MiB) + split-K partials of the hidden layer + q_hat/k_hat; M_hat is not stored
+    assert ws >= 256 * 4096 * 2 + 256 * 256 * 4 + 2 * 256 * 128 * 4
+    assert ws < 256 * 4096 * 2 + 16 * 256 * 256 * 4 + 2 * 256 * 128 * 4
     assert L.lemo_predict_scores_workspace(0, 4096, 64, 128) == 0
 
 
