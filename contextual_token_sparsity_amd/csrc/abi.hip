@@ -280,6 +280,30 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
                        "lemo_gather_pad launch");
 }
 
+lemo_status lemo_gather_pad_multi(int n_src, const lemo_bf16* const* srcs, const int* widths, const int* ld_srcs,
+                                  lemo_bf16* const* dsts, const int* ld_dsts, int n_tokens, int block,
+                                  const int32_t* kept_blocks, const int32_t* n_kept, int cap_rows, int pad_multiple,
+                                  int32_t* dev_status, void* stream) {
+  REQUIRE(n_src >= 1 && n_src <= 4, LEMO_ERR_INVALID_ARG, "n_src %d (1..4)", n_src);
+  REQUIRE(srcs && widths && ld_srcs && dsts && ld_dsts, LEMO_ERR_INVALID_ARG, "an argument array is NULL");
+  REQUIRE(kept_blocks && n_kept, LEMO_ERR_INVALID_ARG, "kept_blocks or n_kept is NULL");
+  REQUIRE(n_tokens > 0 && block > 0 && cap_rows > 0 && pad_multiple > 0, LEMO_ERR_INVALID_ARG,
+          "sizes must be positive (n_tokens=%d block=%d cap_rows=%d pad_multiple=%d)", n_tokens, block, cap_rows,
+          pad_multiple);
+  for (int i = 0; i < n_src; ++i) {
+    REQUIRE(widths[i] > 0, LEMO_ERR_INVALID_ARG, "width of source %d must be positive (got %d)", i, widths[i]);
+    REQUIRE(widths[i] % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d of source %d must be a multiple of 8", widths[i], i);
+    lemo_status st;
+    if ((st = check_rows(srcs[i], ld_srcs[i], widths[i], "src")) != LEMO_OK) return st;
+    if ((st = check_rows(dsts[i], ld_dsts[i], widths[i], "dst")) != LEMO_OK) return st;
+  }
+  return device_status(lemo_launch_gather_multi(n_src, reinterpret_cast<const uint16_t* const*>(srcs), widths,
+                                                ld_srcs, reinterpret_cast<uint16_t* const*>(dsts), ld_dsts, n_tokens,
+                                                block, kept_blocks, n_kept, cap_rows, pad_multiple, dev_status,
+                                                static_cast<hipStream_t>(stream)),
+                       "lemo_gather_pad_multi launch");
+}
+
 // The scatter and the recompute: y holds y_rows rows (INT_MAX: the caller
 // guarantees at least the kept rows).
 static lemo_status scatter_common(const char* fn, lemo_bf16* residual, int n_tokens, int width, int ld_res, int block,

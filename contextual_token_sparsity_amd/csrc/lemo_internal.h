@@ -73,6 +73,12 @@ hipError_t lemo_launch_select(const float* scores, int n_blocks, int mode, float
 hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int ld_src, int block,
                               const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst,
                               int cap_rows, int pad_multiple, int32_t* dev_status, hipStream_t stream);
+// n_src (1..4) matrices gathered on one kept list in one launch (each with its
+// own width, leading dimensions and destination; same cap_rows and padding)
+hipError_t lemo_launch_gather_multi(int n_src, const uint16_t* const* srcs, const int* widths, const int* ld_srcs,
+                                    uint16_t* const* dsts, const int* ld_dsts, int n_tokens, int block,
+                                    const int32_t* kept, const int32_t* n_kept, int cap_rows, int pad_multiple,
+                                    int32_t* dev_status, hipStream_t stream);
 
 // subtract: the backward recompute res -= y instead of res += y.  y holds
 // y_rows rows (kept rows past them are skipped and flag a capacity overflow).

@@ -7,7 +7,7 @@
 //
 // Both kernels are HBM-bound row copies: a workgroup of 256 threads moves a
 // 4 KiB column stripe (256 x 16 bytes) of a row per step, rows are strided
-// over the grid's y dimension, and each thread keeps two rows in flight.
+// over the grid's y dimension, and each thread keeps one or two rows in flight.
 // The number of kept rows is read on the device (it comes from the select
 // step), so the grid is sized for the worst case and idle slots exit.
 #include "lemo_internal.h"
@@ -16,7 +16,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnrollGather = 2;   // rows in flight per thread
-constexpr int kUnrollScatter = 2;
+constexpr int kUnrollScatter = 1;
+constexpr int kRowSlots = 4096;    // the grid's y dimension (row slots)
 
 // Streaming 16-byte accesses: every byte is touched once, so the loads and
 // stores carry the nontemporal hint and do not displace other data from L2
@@ -70,11 +71,24 @@ __device__ __forceinline__ int kept_rows(const int32_t* __restrict__ kept, int n
   return nk * block - short_by;
 }
 
-__global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict__ src, int n_tokens, int width,
-                                                     int ld_src, int block, const int32_t* __restrict__ kept,
-                                                     const int32_t* __restrict__ n_kept_p, uint16_t* __restrict__ dst,
-                                                     int ld_dst, int cap_rows, int pad_multiple,
-                                                     int32_t* __restrict__ status) {
+// Up to kMaxSources matrices gathered on one kept list in one launch: the
+// grid's x dimension is the concatenation of every source's 4 KiB column
+// stripes (source i owns stripes first[i] .. first[i+1]-1).
+constexpr int kMaxSources = 4;
+struct GatherArgs {
+  const uint16_t* src[kMaxSources];
+  uint16_t* dst[kMaxSources];
+  int width[kMaxSources];
+  int ld_src[kMaxSources];
+  int ld_dst[kMaxSources];
+  int first[kMaxSources + 1];
+  int n_src;
+};
+
+__global__ __launch_bounds__(kThreads) void k_gather(GatherArgs g, int n_tokens, int block,
+                                                     const int32_t* __restrict__ kept,
+                                                     const int32_t* __restrict__ n_kept_p, int cap_rows,
+                                                     int pad_multiple, int32_t* __restrict__ status) {
   const int nb = (n_tokens + block - 1) / block;
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
@@ -87,7 +101,15 @@ __global__ __launch_bounds__(kThreads) void k_gather(const uint16_t* __restrict_
     if (n_pad > cap_rows) flags |= LEMO_DEV_CAP_OVERFLOW;
     if (flags) atomicOr(status, flags);
   }
-  const int ch = blockIdx.x * kThreads + threadIdx.x;
+  // which source this workgroup's stripe belongs to (uniform)
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxSources; ++i)
+    if (i < g.n_src && (int)blockIdx.x >= g.first[i]) si = i;
+  const uint16_t* __restrict__ src = g.src[si];
+  uint16_t* __restrict__ dst = g.dst[si];
+  const int width = g.width[si], ld_src = g.ld_src[si], ld_dst = g.ld_dst[si];
+  const int ch = ((int)blockIdx.x - g.first[si]) * kThreads + threadIdx.x;
   if (ch * 8 >= width) return;
   const int step = gridDim.y;
   for (int p0 = blockIdx.y; p0 < rows; p0 += step * kUnrollGather) {
@@ -162,28 +184,53 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
   }
 }
 
-// Workgroups: one per 4 KiB column stripe (x) times 8192 row slots (y, fewer
-// when there are fewer rows), each thread keeping two rows in flight.
-// Measured on the 7B shape with the source streaming from HBM, this beats
-// 1024 slots with 8 rows in flight by up to 12% (a plain streaming copy runs
-// at about 5.5 TB/s here).  The slot count does not grow with the capacity:
-// the number of kept rows is only known on the device, and a grid sized for
-// every possible row left most workgroups idle (each still reads n_kept),
-// which cost a 4096-wide gather a third of its rate.
+// Workgroups: one per 4 KiB column stripe (x) times 4096 row slots (y,
+// fewer when there are fewer rows).  A sweep on the 7B shape (110 of 256
+// blocks kept, 7040 rows; sources rotated over three copies so that they
+// stream from HBM; back-to-back launches) over 1024..8192 slots and 1, 2 or
+// 4 rows in flight per thread: 4096 slots with two rows in flight for the
+// gathers (X 70%, the MLP activation 70%, both in one launch 75% of 8 TB/s)
+// and one row for the scatter (75%); 8192 slots were 3-9 points slower.  (A
+// plain streaming copy peaks at 78% here, a read at 86%, a write at 70%.)
+// The slot count does not grow with the capacity: the number of kept rows is
+// only known on the device, and a grid sized for every possible row leaves
+// most workgroups idle (each still reads n_kept).
 dim3 grid_for(int width, int max_rows) {
   const int gx = (width / 8 + kThreads - 1) / kThreads;
-  const int gy = max(1, min(max_rows, 8192));
+  const int gy = max(1, min(max_rows, kRowSlots));
   return dim3(gx, gy);
 }
 
 }  // namespace
 
+hipError_t lemo_launch_gather_multi(int n_src, const uint16_t* const* srcs, const int* widths, const int* ld_srcs,
+                                    uint16_t* const* dsts, const int* ld_dsts, int n_tokens, int block,
+                                    const int32_t* kept, const int32_t* n_kept, int cap_rows, int pad_multiple,
+                                    int32_t* dev_status, hipStream_t stream) {
+  GatherArgs g = {};
+  g.n_src = n_src;
+  int stripes = 0;
+  for (int i = 0; i < n_src; ++i) {
+    g.src[i] = srcs[i];
+    g.dst[i] = dsts[i];
+    g.width[i] = widths[i];
+    g.ld_src[i] = ld_srcs[i];
+    g.ld_dst[i] = ld_dsts[i];
+    g.first[i] = stripes;
+    stripes += grid_for(widths[i], 1).x;
+  }
+  g.first[n_src] = stripes;
+  const dim3 grid(stripes, grid_for(8, cap_rows).y);
+  hipLaunchKernelGGL(k_gather, grid, dim3(kThreads), 0, stream, g, n_tokens, block, kept, n_kept, cap_rows,
+                     pad_multiple, dev_status);
+  return hipGetLastError();
+}
+
 hipError_t lemo_launch_gather(const uint16_t* src, int n_tokens, int width, int ld_src, int block,
                               const int32_t* kept, const int32_t* n_kept, uint16_t* dst, int ld_dst, int cap_rows,
                               int pad_multiple, int32_t* dev_status, hipStream_t stream) {
-  hipLaunchKernelGGL(k_gather, grid_for(width, cap_rows), dim3(kThreads), 0, stream, src, n_tokens, width,
-                     ld_src, block, kept, n_kept, dst, ld_dst, cap_rows, pad_multiple, dev_status);
-  return hipGetLastError();
+  return lemo_launch_gather_multi(1, &src, &width, &ld_src, &dst, &ld_dst, n_tokens, block, kept, n_kept, cap_rows,
+                                  pad_multiple, dev_status, stream);
 }
 
 hipError_t lemo_launch_scatter(uint16_t* res, int n_tokens, int width, int ld_res, int block, const int32_t* kept,

@@ -5,25 +5,48 @@
 // One workgroup of 1024 threads (16 waves) handles up to 8192 blocks:
 //   * scores are staged in LDS;
 //   * the threshold is the caller's, the mean (float64 sum in block order by
-//     one lane, then divided and rounded to fp32), or implied by top-k: the
-//     rank of block c is the number of blocks that beat it (higher score, or
-//     equal score and lower index; NaN loses to every number);
+//     one lane, then divided and rounded to fp32), or implied by top-k;
+//   * top-k: every score becomes an order-preserving 32-bit key (larger key
+//     = better score; -0 and +0 share a key as they compare equal; NaN gets
+//     the lowest key, below -inf), and the k-th largest key T is found by a
+//     radix select in LDS: four rounds of 8 bits, each a histogram of the
+//     keys that match the digits chosen so far and a scan of its 256 bins
+//     from the top.  The result is the keys above T plus, among the blocks
+//     whose key is T, the ones with the lowest indices (ties go to the lower
+//     block index), as many as k still needs; the reported threshold is the
+//     score of the last of them, the k-th best.  (This replaced ranking
+//     every block by counting the blocks that beat it, O(nb^2).)
 //   * the ascending kept list is built 1024 blocks at a time: a wave ballot
 //     of the keep bits, the lane's prefix from the bits below it (mbcnt), and
-//     the waves' counts scanned through LDS.
+//     the waves' counts scanned through LDS; ties at T are counted the same
+//     way in block order.
 #include "lemo_internal.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 8192;
 constexpr int kPerThread = kMaxBlocks / kThreads;
 
-__device__ __forceinline__ bool beats(float a, int ia, float b, int ib) {
-  const bool an = a != a, bn = b != b;
-  if (an != bn) return bn;
-  if (!an && a != b) return a > b;
-  return ia < ib;
+// Order-preserving key of a score: a > b as floats iff key(a) > key(b);
+// equal floats (including -0 and +0) share a key; every NaN gets 0, below
+// the key of -inf (0x007fffff).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0u;   // NaN
+  if ((b & 0x7fffffffu) == 0u) b = 0u;              // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Sum of `v` over the lanes below this one plus this one (inclusive scan).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
 }
 
 __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ scores, int nb, int mode,
@@ -31,7 +54,12 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
                                                      int32_t* __restrict__ kept, int32_t* __restrict__ n_kept,
                                                      float* __restrict__ theta_out, int32_t* __restrict__ status) {
   __shared__ float s[kMaxBlocks];
-  __shared__ int wave_cnt[kThreads / 64];
+  __shared__ int wave_cnt[kWaves];
+  __shared__ int tie_cnt[kWaves];
+  __shared__ uint32_t hist[256];
+  __shared__ int scan_tot[4];
+  __shared__ uint32_t sel_key;
+  __shared__ int sel_rem;
   __shared__ float theta_sh;
   __shared__ int nonfinite;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -49,43 +77,95 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
   if (bad) atomicOr(&nonfinite, 1);
   __syncthreads();
 
-  uint32_t topk_bits = 0;
+  const bool topk = mode == 1 && keep > 0;
+  uint32_t key[kPerThread];
+  uint32_t T = 0;       // top-k: the k-th largest key
+  int ties_kept = 0;    // top-k: how many blocks with key T are kept
   if (mode == 2) {
     if (tid == 0) {
       double acc = 0.0;
       for (int c = 0; c < nb; ++c) acc += (double)s[c];
       theta_sh = (float)(acc / (double)nb);
     }
-  } else if (mode == 1) {
-#pragma unroll 1
+  } else if (topk) {
+#pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
       const int c = tid + j * kThreads;
-      if (c >= nb) break;
-      const float v = s[c];
-      int rank = 0;
-      for (int o = 0; o < nb; ++o) rank += beats(s[o], o, v, c) ? 1 : 0;
-      if (rank < keep) topk_bits |= 1u << j;
-      if (rank == keep - 1) theta_sh = v;  // exactly one block has this rank
+      key[j] = c < nb ? order_key(s[c]) : 0u;
     }
+    uint32_t prefix = 0;
+    int rem = keep;                 // blocks still to take at or below the digits chosen so far
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t hmask = shift == 24 ? 0u : ~((1u << (shift + 8)) - 1u);   // digits already chosen
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < nb && (key[j] & hmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      // threads 0..255 take the bins from the top (bin 255 - tid): an
+      // inclusive scan gives the count of keys with this digit or a larger one
+      int h = 0, incl = 0;
+      if (tid < 256) {
+        h = (int)hist[255 - tid];
+        incl = wave_incl_scan(h, lane);
+        if (lane == 63) scan_tot[wave] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        for (int w = 0; w < wave; ++w) incl += scan_tot[w];
+        const int excl = incl - h;
+        if (excl < rem && rem <= incl) {   // exactly one bin
+          sel_key = prefix | ((uint32_t)(255 - tid) << shift);
+          sel_rem = rem - excl;
+        }
+      }
+      __syncthreads();
+      prefix = sel_key;
+      rem = sel_rem;
+    }
+    T = prefix;
+    ties_kept = rem;
   }
   __syncthreads();
   const float theta = theta_sh;
 
-  int base = 0;
+  int base = 0, tie_base = 0;
   for (int j = 0; j * kThreads < nb; ++j) {
     const int c = tid + j * kThreads;
     bool k = false;
-    if (c < nb) {
-      k = (mode == 1) ? ((topk_bits >> j) & 1u) : (s[c] >= theta);
-      mask[c] = k ? 1 : 0;
+    if (mode == 1) {
+      // rank of this block among the blocks with key T, in block order
+      const bool tie = topk && c < nb && key[j] == T;
+      const unsigned long long tb = __ballot(tie);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(tb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)tb, 0));
+      if (lane == 0) tie_cnt[wave] = __popcll(tb);
+      __syncthreads();
+      int woff = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int cw = tie_cnt[w];
+        woff += (w < wave) ? cw : 0;
+        total += cw;
+      }
+      const int rank = tie_base + woff + below;
+      k = topk && c < nb && (key[j] > T || (tie && rank < ties_kept));
+      if (tie && rank == ties_kept - 1) theta_sh = s[c];   // the k-th best block
+      tie_base += total;
+    } else if (c < nb) {
+      k = s[c] >= theta;
     }
+    if (c < nb) mask[c] = k ? 1 : 0;
     const unsigned long long bal = __ballot(k);
     const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
     if (lane == 0) wave_cnt[wave] = __popcll(bal);
     __syncthreads();
     int woff = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const int cw = wave_cnt[w];
       woff += (w < wave) ? cw : 0;
       total += cw;
@@ -96,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
   }
   if (tid == 0) {
     *n_kept = base;
-    if (theta_out) *theta_out = theta;
+    if (theta_out) *theta_out = theta_sh;
     if (status && nonfinite) atomicOr(status, LEMO_DEV_NONFINITE);
   }
 }

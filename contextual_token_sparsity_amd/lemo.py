@@ -38,6 +38,7 @@ _SIGS = {
     "lemo_gather_pad": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "lemo_scatter_residual": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "lemo_residual_recompute": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp]),
+    "lemo_gather_pad_multi": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp]),
     "lemo_scatter_residual_capped": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "lemo_residual_recompute_capped": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _i, _i, _vp, _vp]),
     "lemo_mlp_block_scores_workspace": (_sz, [_i, _i, _i]),
@@ -317,6 +318,36 @@ def lemo_gather_pad(src, block: int, kept_blocks, n_kept, dst, pad_multiple: int
                                _ld(dst), dst.shape[0], pad_multiple, _ptr(dev_status), _stream(src.device))
     _check(st, "lemo_gather_pad")
     return dst
+
+
+def lemo_gather_pad_multi(srcs, dsts, block: int, kept_blocks, n_kept, pad_multiple: int = 1, widths=None,
+                          n_tokens: int = None, dev_status=None):
+    """Selective load of up to 4 matrices on one kept list in one launch:
+    dsts[i] receives what lemo_gather_pad(srcs[i], ...) would write.  The
+    capacity is the smallest destination's row count."""
+    if not 1 <= len(srcs) == len(dsts) <= 4:
+        raise ValueError("1 to 4 sources, one destination each")
+    for t in list(srcs) + list(dsts):
+        _bf16(t)
+    ws = [t.shape[1] for t in srcs] if widths is None else list(widths)
+    n = srcs[0].shape[0] if n_tokens is None else n_tokens
+    for i, (a, b_) in enumerate(zip(srcs, dsts)):
+        _rows_within(a, n, ws[i], f"srcs[{i}]")
+        _rows_within(b_, 0, ws[i], f"dsts[{i}]")
+        if a.device != srcs[0].device or b_.device != srcs[0].device:
+            raise ValueError("all matrices must be on one device")
+    _kept_bufs(kept_blocks, n_kept, dev_status, srcs[0].device)
+    k = len(srcs)
+    arr_p = (ctypes.c_void_p * k)(*[t.data_ptr() for t in srcs])
+    arr_d = (ctypes.c_void_p * k)(*[t.data_ptr() for t in dsts])
+    arr_w = (ctypes.c_int * k)(*ws)
+    arr_ls = (ctypes.c_int * k)(*[_ld(t) for t in srcs])
+    arr_ld = (ctypes.c_int * k)(*[_ld(t) for t in dsts])
+    cap = min(t.shape[0] for t in dsts)
+    st = lib().lemo_gather_pad_multi(k, arr_p, arr_w, arr_ls, arr_d, arr_ld, n, block, _ptr(kept_blocks),
+                                     _ptr(n_kept), cap, pad_multiple, _ptr(dev_status), _stream(srcs[0].device))
+    _check(st, "lemo_gather_pad_multi")
+    return dsts
 
 
 def _scatter(fn, residual, block, kept_blocks, n_kept, y, width, n_tokens, dev_status, y_rows):

@@ -270,6 +270,27 @@ lemo_status lemo_gather_pad(const lemo_bf16* src, int n_tokens, int width, int l
                             void* stream);
 
 /* ------------------------------------------------------------------------
+ * Selective load of several matrices on one kept list in one launch (Jenga
+ * 4.2.3, selective load: a layer reads the kept tokens of every matrix it
+ * consumes, e.g. the attention input and the MLP activation, from their
+ * original rows).  For each source i < n_src the result is exactly that of
+ * lemo_gather_pad(srcs[i], n_tokens, widths[i], ld_srcs[i], block, ...,
+ * dsts[i], ld_dsts[i], cap_rows, pad_multiple): the same rows, zero padding,
+ * untouched rows past the padding, capacity and status behaviour.
+ *  n_src          1..4.
+ *  srcs, widths, ld_srcs, dsts, ld_dsts   host arrays of n_src entries; the
+ *                 matrices they point to are device memory.  Every dsts[i]
+ *                 holds at least cap_rows rows; no destination may overlap
+ *                 any source or another destination.
+ * Errors: INVALID_ARG (NULL, sizes, n_src, ld < width), ALIGNMENT (pointers,
+ * ld, width).
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_gather_pad_multi(int n_src, const lemo_bf16* const* srcs, const int* widths, const int* ld_srcs,
+                                  lemo_bf16* const* dsts, const int* ld_dsts, int n_tokens, int block,
+                                  const int32_t* kept_blocks, const int32_t* n_kept, int cap_rows, int pad_multiple,
+                                  int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
  * Token movement fused into the layer's products (Jenga 4.2.3, permutation-
  * free token movement, Figure 18: selective load and in-place addition are
  * carried out inside the computation, not as separate passes).

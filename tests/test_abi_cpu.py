@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
 
@@ -237,6 +237,29 @@ def test_scatter_capped_rejects(L, kw, status, recompute):
     assert lemo.lemo_last_error()
     if kw == dict(rows=-1):
         assert "y_rows" in lemo.lemo_last_error()
+
+
+def gm(L, n_src=2, srcs=(P, P), widths=(512, 64), lds=(512, 64), dsts=(P, P), ldd=(512, 64), n=1024, b=64,
+       kept=P, nk=P, cap=256, pad=1):
+    k = 2
+    arr = lambda t, vals: (t * k)(*vals) if vals is not None else None
+    return L.lemo_gather_pad_multi(n_src, arr(ctypes.c_void_p, srcs), arr(ctypes.c_int, widths),
+                                   arr(ctypes.c_int, lds), arr(ctypes.c_void_p, dsts), arr(ctypes.c_int, ldd), n, b,
+                                   kept, nk, cap, pad, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_src=0), INVALID), (dict(n_src=5), INVALID), (dict(srcs=None), INVALID), (dict(kept=NULL), INVALID),
+    (dict(cap=0), INVALID), (dict(pad=0), INVALID), (dict(srcs=(P, NULL)), INVALID), (dict(dsts=(NULL, P)), INVALID),
+    (dict(widths=(512, 0)), INVALID), (dict(ldd=(512, 32)), INVALID),
+    (dict(widths=(512, 60), lds=(512, 64), ldd=(512, 64)), ALIGN), (dict(dsts=(P, P2)), ALIGN),
+    (dict(lds=(516, 64)), ALIGN),
+])
+def test_gather_multi_rejects(L, kw, status):
+    """The multi-source gather checks every source and destination as the
+    single gather does, and its source count (1..4)."""
+    assert gm(L, **kw) == status
+    assert lemo.lemo_last_error()
 
 
 def test_fused_tile_limit(L):

@@ -658,6 +658,72 @@ def test_gather_scatter(case):
     assert int(status.item()) == 0
 
 
+GATHER_MULTI = [
+    # (N, block, keep fraction, pad_multiple, extra cap rows, [(width, ld_src, ld_dst), ...])
+    (1024, 64, 0.5, 256, 8, [(512, 520, 512), (64, 64, 72)]),
+    (2048, 16, 0.3, 7, 3, [(8, 16, 8), (2056, 2056, 2064), (1376, 1376, 1376)]),
+    (1000, 64, 1.0, 64, 0, [(256, 256, 256), (4096, 4096, 4096), (8, 8, 8), (11008, 11008, 11008)]),  # ragged N
+    (1024, 64, 0.0, 256, 5, [(128, 128, 128), (64, 64, 64)]),                                       # keep none
+]
+
+
+@pytest.mark.parametrize("case", GATHER_MULTI, ids=lambda c: "N%d_b%d_keep%.2f_src%d" % (c[0], c[1], c[2], len(c[5])))
+def test_gather_multi(case):
+    """Several matrices gathered on one kept list in one launch: each
+    destination bit-exact against the oracle's gather of that source
+    (padding, rows past it left as they were, a ragged last block)."""
+    n, b, frac, pad, extra, mats = case
+    say("gather multi", case)
+    rng = np.random.default_rng(n + len(mats))
+    nb = -(-n // b)
+    kept = _kept_from_mask(rng, nb, frac)
+    nk = kept.size
+    R = O.kept_token_rows(kept, nk, b, n).size
+    cap = max(1, -(-R // pad) * pad + extra)
+    kept_d = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    kept_d[:nk] = torch.from_numpy(kept).cuda()
+    nk_d = torch.tensor([nk], dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    srcs, dsts, refs = [], [], []
+    for w, lds, ldd in mats:
+        src = synth.random_bf16(rng, (n, w))
+        sentinel = np.full((cap, w), 0x5A5A, np.uint16)
+        ref, over = O.gather_pad(src, b, kept, nk, sentinel, pad)
+        assert not over
+        srcs.append(padded(src, lds, 0x7FC0))
+        dsts.append(padded(sentinel, ldd, 0x1234))
+        refs.append(ref)
+    lemo.lemo_gather_pad_multi([sd[:, :w] for sd, (w, _, _) in zip(srcs, mats)],
+                               [dd[:, :w] for dd, (w, _, _) in zip(dsts, mats)], b, kept_d, nk_d, pad_multiple=pad,
+                               n_tokens=n, dev_status=status)
+    for dd, ref, (w, _, _) in zip(dsts, refs, mats):
+        got = host_bits(dd)
+        assert np.array_equal(got[:, :w], ref)
+        assert np.all(got[:, w:] == 0x1234)
+    assert int(status.item()) == 0
+
+
+def test_gather_multi_full_size_oracle_mask():
+    """X and the MLP activation of the 7B N=16K layer gathered in one launch
+    on the oracle's predicted mask (MEAN), padded to 256 rows: bit-exact."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    say("gather multi full size")
+    L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, rank=w.rank, mlp_width=w.mlp_width,
+                         planted_frac=w.planted_frac, with_y=False)
+    _, I_ref, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
+    _, kept, nk, _ = O.select_mask(I_ref.astype(np.float32), O.SELECT_MEAN)
+    cap = -(-(nk * w.block) // 256) * 256
+    dx = torch.empty((cap, w.d_model), dtype=torch.int16, device="cuda")
+    da = torch.empty((cap, w.mlp_width), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lemo.lemo_gather_pad_multi([dev(L.x), dev(L.act)], [dx, da], w.block, dev(kept), dev(np.array([nk], np.int32)),
+                               pad_multiple=256, dev_status=status)
+    for src, dd, width in ((L.x, dx, w.d_model), (L.act, da, w.mlp_width)):
+        ref, _ = O.gather_pad(src, w.block, kept, nk, np.zeros((cap, width), np.uint16), 256)
+        assert np.array_equal(host_bits(dd), ref)
+    assert int(status.item()) == 0
+
+
 @pytest.mark.parametrize("case", MOVE, ids=lambda c: "N%d_w%d_b%d_keep%.2f" % (c[0], c[1], c[4], c[5]))
 def test_residual_recompute(case):
     """Backward recompute, bit for bit against the oracle on an independent
