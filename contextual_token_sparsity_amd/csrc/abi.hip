@@ -191,10 +191,10 @@ size_t lemo_predict_scores_workspace(int n_tokens, int d_model, int block, int r
   return lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
 }
 
-lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
-                                const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
-                                const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by lemo_predict_scores and lemo_predict_scores_noalloc.
+static lemo_status predict_checks(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                  const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                  const lemo_bf16* v_k, int rank, const float* scores) {
   REQUIRE(scores != nullptr && u_q && v_q && u_k && v_k, LEMO_ERR_INVALID_ARG, "scores or a predictor matrix is NULL");
   REQUIRE(n_tokens > 0 && block > 0 && d_model > 0 && rank > 0, LEMO_ERR_INVALID_ARG,
           "sizes must be positive (n_tokens=%d block=%d d_model=%d rank=%d)", n_tokens, block, d_model, rank);
@@ -207,6 +207,15 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
           "predictor matrices must be 16-byte aligned");
+  return LEMO_OK;
+}
+
+lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  lemo_status st = predict_checks(x, n_tokens, d_model, ld_x, block, u_q, v_q, u_k, v_k, rank, scores);
+  if (st != LEMO_OK) return st;
   const size_t need = lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
   REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
           "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -214,6 +223,25 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
   return device_status(lemo_launch_predict(x, n_tokens, d_model, ld_x, block, u_q, v_q, u_k, v_k, rank, block_scores,
                                            scores, workspace, static_cast<hipStream_t>(stream)),
                        "lemo_predict_scores launch");
+}
+
+lemo_status lemo_predict_scores_noalloc(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                        const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                        const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
+                                        void* stream) {
+  lemo_status st = predict_checks(x, n_tokens, d_model, ld_x, block, u_q, v_q, u_k, v_k, rank, scores);
+  if (st != LEMO_OK) return st;
+  const size_t need = lemo_predict_ws_bytes(n_tokens, d_model, block, rank);
+  REQUIRE(need <= lemo_predict_static_capacity(), LEMO_ERR_UNSUPPORTED,
+          "this shape needs %zu bytes of scratch; the static scratch holds %zu (use lemo_predict_scores with a "
+          "workspace)", need, lemo_predict_static_capacity());
+  void* scratch = nullptr;
+  if ((st = device_status(lemo_predict_static_scratch(&scratch), "lemo_predict_scores_noalloc scratch lookup")) !=
+      LEMO_OK)
+    return st;
+  return device_status(lemo_launch_predict(x, n_tokens, d_model, ld_x, block, u_q, v_q, u_k, v_k, rank, block_scores,
+                                           scores, scratch, static_cast<hipStream_t>(stream)),
+                       "lemo_predict_scores_noalloc launch");
 }
 
 size_t lemo_token_embeddings_workspace(int n_tokens, int d_model, int rank) {

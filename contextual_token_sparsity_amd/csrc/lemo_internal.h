@@ -51,6 +51,11 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
                                const uint16_t* v_k, int rank, float* m_out, float* scores,
                                void* workspace, hipStream_t stream);
 
+// lemo_predict_scores_noalloc: capacity of the static scratch array, and its
+// device address on the current device (looked up once per device)
+size_t lemo_predict_static_capacity();
+hipError_t lemo_predict_static_scratch(void** ptr);
+
 size_t lemo_token_ws_bytes(int n_tokens, int d_model, int rank);
 hipError_t lemo_launch_token_embed(const uint16_t* x, int n_tokens, int d_model, int ld_x, const uint16_t* u_q,
                                    const uint16_t* v_q, const uint16_t* u_k, const uint16_t* v_k, int rank,

@@ -15,6 +15,8 @@
 //                 q_hat = hid_q V_q (stored transposed), k_hat = hid_k V_k in fp32
 //   k_pair_colsum I_hat[n] = sum_m max(0, q_hat[m] . k_hat[n]) in a fixed
 //                 order; M_hat is written only when the caller asks for it.
+#include <mutex>
+
 #include "lemo_internal.h"
 
 namespace {
@@ -279,7 +281,41 @@ Layout layout(int n_tokens, int d_model, int block, int rank) {
   return L;
 }
 
+// Scratch of lemo_predict_scores_noalloc: a fixed device array instead of a
+// caller workspace, for callers that cannot allocate.  Each device that loads
+// the library holds its own copy for the life of the process.  Host code
+// never uses the array's name as an address: the device address is fetched
+// once per device with hipGetSymbolAddress (with that device current) and
+// kept in g_static_ptr.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+size_t lemo_predict_static_capacity() { return kStaticScratchBytes; }
+
+// Device address of the current device's scratch array (looked up on the
+// first call for that device).
+hipError_t lemo_predict_static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_static_ptr[dev] = p;
+  }
+  *ptr = g_static_ptr[dev];
+  return hipSuccess;
+}
 
 // Number of d_model slices for the hidden product: each workgroup takes one
 // slice of d_model (split over its 4 waves in multiples of 16).  Enough

@@ -32,6 +32,7 @@ _SIGS = {
                                        _vp, _vp, _vp, _sz, _vp]),
     "lemo_predict_scores_workspace": (_sz, [_i, _i, _i, _i]),
     "lemo_predict_scores": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "lemo_predict_scores_noalloc": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "lemo_token_embeddings_workspace": (_sz, [_i, _i, _i]),
     "lemo_token_embeddings": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "lemo_select_mask": (_i, [_vp, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -245,6 +246,34 @@ def lemo_predict_scores(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, 
                                    _ptr(block_scores), _ptr(scores), _ptr(workspace), _ws_bytes(workspace, x.device),
                                    _stream(x.device))
     _check(st, "lemo_predict_scores")
+    return scores, block_scores
+
+
+def lemo_predict_scores_noalloc(x, u_q, v_q, u_k, v_k, block: int, d_model: int = None, block_scores=None,
+                                scores=None):
+    """lemo_predict_scores with the library's fixed per-device scratch instead
+    of a workspace (the library allocates nothing; shapes needing more than
+    its 16 MiB are refused).  Calls that overlap on one device race.
+    Returns (scores [nb] fp32, block_scores or None)."""
+    for t in (x, u_q, v_q, u_k, v_k):
+        _bf16(t)
+    n = x.shape[0]
+    d = x.shape[1] if d_model is None else d_model
+    rank = u_q.shape[1]
+    if block <= 0:
+        raise ValueError(f"block must be positive (got {block})")
+    nb = -(-n // block)
+    _rows_within(x, n, d, "x")
+    for name, t, r, c in (("u_q", u_q, d, rank), ("u_k", u_k, d, rank), ("v_q", v_q, rank, rank),
+                          ("v_k", v_k, rank, rank)):
+        _buf(t, t.dtype, r * c, name, x.device)
+    if scores is None:
+        scores = torch.empty(nb, dtype=torch.float32, device=x.device)
+    _buf(scores, torch.float32, nb, "scores", x.device)
+    _buf(block_scores, torch.float32, nb * nb, "block_scores", x.device)
+    st = lib().lemo_predict_scores_noalloc(_ptr(x), n, d, _ld(x), block, _ptr(u_q), _ptr(v_q), _ptr(u_k),
+                                           _ptr(v_k), rank, _ptr(block_scores), _ptr(scores), _stream(x.device))
+    _check(st, "lemo_predict_scores_noalloc")
     return scores, block_scores
 
 

@@ -198,6 +198,27 @@ lemo_status lemo_predict_scores(const lemo_bf16* x, int n_tokens, int d_model, i
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * lemo_predict_scores without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * lemo_predict_scores, minus the workspace: the scratch is a fixed 16 MiB
+ * array in the library's device code, one per device, held until the process
+ * ends.  The call allocates nothing.
+ *  Limit: shapes whose lemo_predict_scores_workspace() exceeds 16 MiB (16 *
+ *  2^20 bytes) are refused with LEMO_ERR_UNSUPPORTED; e.g. 16384 tokens of
+ *  4096 in blocks of 64 with rank 128 need 4.3 MiB, 32768 tokens of 5120 in
+ *  blocks of 128 with rank 256 need 5 MiB.
+ *  Every call on one device shares that device's array: calls that overlap
+ *  on one device (on different streams, or from several threads without
+ *  ordering) race and give unspecified results.  No part of the scratch
+ *  needs to start at zero.
+ * ------------------------------------------------------------------------ */
+lemo_status lemo_predict_scores_noalloc(const lemo_bf16* x, int n_tokens, int d_model, int ld_x, int block,
+                                        const lemo_bf16* u_q, const lemo_bf16* v_q, const lemo_bf16* u_k,
+                                        const lemo_bf16* v_k, int rank, float* block_scores, float* scores,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-token predictor embeddings (Jenga 4.2.2, Figure 8, and its complexity
  * analysis, which prices the query and key predictors at one pass per token).
  *

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = lemo.declared_symbols()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
 
@@ -260,6 +260,22 @@ def test_gather_multi_rejects(L, kw, status):
     single gather does, and its source count (1..4)."""
     assert gm(L, **kw) == status
     assert lemo.lemo_last_error()
+
+
+def test_predict_noalloc_checks(L):
+    """The no-allocation predictor checks what lemo_predict_scores checks and
+    refuses shapes whose scratch would exceed its fixed 16 MiB, before any
+    device call."""
+    call = lambda n=16384, d=4096, b=64, r=128, x=P, I=P: L.lemo_predict_scores_noalloc(
+        x, n, d, d, b, P, P, P, P, r, NULL, I, NULL)
+    assert call(x=NULL) == INVALID
+    assert call(I=NULL) == INVALID
+    assert call(r=48) == UNSUP
+    assert call(b=3) == UNSUP
+    assert call(n=4096 * 64, d=4096) == UNSUP               # 4096 blocks: x-bar alone is 32 MiB
+    assert "16777216" in lemo.lemo_last_error()
+    assert L.lemo_predict_scores_workspace(16384, 4096, 64, 128) <= 16 << 20
+    assert L.lemo_predict_scores_workspace(32768, 5120, 128, 256) <= 16 << 20
 
 
 def test_fused_tile_limit(L):
