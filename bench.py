@@ -8,7 +8,7 @@ host synchronisation inside the step:
   1. lemo_block_scores     exact block scores of Q K^T (Eq. 2 head reduction)
   2. lemo_predict_scores   predicted block scores from X (Eq. 3)
   3. lemo_select_mask      mean threshold on the predicted scores (Alg. 1 step 1)
-  4. lemo_gather_pad x2    kept rows of X and of the MLP activation, padded to 256
+  4. lemo_gather_pad_multi kept rows of X and of the MLP activation (one launch), padded to 256
   5. lemo_scatter_residual layer output of the kept rows added into the residual
 Inputs are generated (seeded, synthetic) and resident in device memory before
 the timed region.  Reported value: tokens scored + eliminated per second.
@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle's exact scores over every query block (minutes) instead of a sample")
     ap.add_argument("--head-reduce", choices=["paper", "headmax"], default="paper")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
@@ -128,10 +130,7 @@ def main():
                               threshold_used=theta, dev_status=status)
         if timed:
             mark("select1")
-        lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256, dev_status=status)
-        if timed:
-            mark("gatherx1")
-        lemo.lemo_gather_pad(act, b, kept, n_kept, ak, pad_multiple=256, dev_status=status)
+        lemo.lemo_gather_pad_multi([x, act], [xk, ak], b, kept, n_kept, pad_multiple=256, dev_status=status)
         if timed:
             mark("gather1")
         lemo.lemo_scatter_residual(resid, b, kept, n_kept, y, dev_status=status)
@@ -186,12 +185,7 @@ def main():
     bytes_ga = 2 * R * wm * 2 + (Rp - R) * wm * 2
     bytes_sc = 3 * R * d * 2
     move_bytes = bytes_gx + bytes_ga + bytes_sc
-    warm_ms = {"gather_x": avg("select1", "gatherx1"), "gather_act": avg("gatherx1", "gather1"),
-               "scatter": stages["scatter_residual"]}
-    cold_ms = movement_cold(lambda: lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256),
-                            lambda: lemo.lemo_gather_pad(act, b, kept, n_kept, ak, pad_multiple=256),
-                            lambda: lemo.lemo_scatter_residual(resid, b, kept, n_kept, y), stream, dev)
-    move_bytes_k = {"gather_x": bytes_gx, "gather_act": bytes_ga, "scatter": bytes_sc}
+    warm_ms = {"gather_x_and_act": stages["gather_pad_x_and_act"], "scatter": stages["scatter_residual"]}
     out = {
         "metric": METRIC,
         "value": N * args.steps / (total_ms * 1e-3),
@@ -224,18 +218,18 @@ def main():
         "stages_ms": stages,
         "n_kept_blocks": nk,
         "movement_GBps": move_bytes / ((stages["gather_pad_x_and_act"] + stages["scatter_residual"]) * 1e-3) / 1e9,
-        "movement": {
-            kname: {"bytes": move_bytes_k[kname],
-                    "warm_GBps": move_bytes_k[kname] / (warm_ms[kname] * 1e-3) / 1e9,
-                    "cold_GBps": move_bytes_k[kname] / (cold_ms[kname] * 1e-3) / 1e9,
-                    "cold_frac": move_bytes_k[kname] / (cold_ms[kname] * 1e-3) / 1e9 / PEAK_HBM_GBS}
-            for kname in ("gather_x", "gather_act", "scatter")},
+        "movement_in_step": {
+            "gather_x_and_act": {"bytes": bytes_gx + bytes_ga,
+                                 "GBps": (bytes_gx + bytes_ga) / (warm_ms["gather_x_and_act"] * 1e-3) / 1e9},
+            "scatter": {"bytes": bytes_sc, "GBps": bytes_sc / (warm_ms["scatter"] * 1e-3) / 1e9}},
         "predictor_path_tokens_per_s": N / (sum(v for kk, v in stages.items() if kk != "block_scores") * 1e-3),
-        "tokens_per_s_without_mlp_gather": N / ((ms_step - warm_ms["gather_act"]) * 1e-3),
         "dev_status": st,
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
     }
+    out["movement"] = movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev)
+    out["chain_13b"] = chain_13b(stream, dev)
+    out["select_topk"] = select_topk(stream, dev)
     out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
     out["other_head_reduce"] = other_head_reduce(q, k, N, H, hd, b, mode, stream, dev)
     out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
@@ -255,7 +249,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_probe_GBps"] = 2.0 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(L, w)
+        out["cpu_baseline"] = cpu_baseline(L, w, full=args.cpu_full)
     print(json.dumps(out), flush=True)
 
 
@@ -476,64 +470,230 @@ def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
     return res
 
 
-def movement_cold(gx, ga, sc, stream, dev, reps=5):
-    """Median time (ms) of each movement call with the 256 MB Infinity Cache
-    flushed first: a 512 MiB buffer is read (not written, so no dirty lines
-    are left to be written back during the timed call) before every launch."""
+def movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev, reps=30):
+    """Each movement call on the step's mask, launched back to back `reps`
+    times with the source rotated over three copies (so every launch reads
+    data it last touched two launches earlier, more than the 256 MB Infinity
+    Cache ago: the reads stream from HBM).  Mean event time per call;
+    algorithmic bytes as in the step (a gathered row read and written once, a
+    pad row written once, a scattered row read twice and written once).
+    `copy_ceiling` is the same gather kernel on a keep-all list: a plain
+    contiguous copy of X, the streaming-copy rate this part reaches with these
+    kernels, beside torch's device-to-device copy of the same bytes."""
     import torch
-    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev).view(torch.int64)
-    res = {}
-    for name, fn in (("gather_x", gx), ("gather_act", ga), ("scatter", sc)):
-        ts = []
+    from contextual_token_sparsity_amd import lemo
+    R = nk * b
+    Rp = -(-R // 256) * 256
+    xs = [x] + [x.clone() for _ in range(2)]
+    acts = [act] + [act.clone() for _ in range(2)]
+    res = [x.clone() for _ in range(3)]
+    xk = torch.empty((Rp, d), dtype=torch.int16, device=dev)
+    ak = torch.empty((Rp, wm), dtype=torch.int16, device=dev)
+    calls = {
+        "gather_x": (2 * R * d * 2 + (Rp - R) * d * 2,
+                     lambda c: lemo.lemo_gather_pad(xs[c], b, kept, n_kept, xk, pad_multiple=256)),
+        "gather_act": (2 * R * wm * 2 + (Rp - R) * wm * 2,
+                       lambda c: lemo.lemo_gather_pad(acts[c], b, kept, n_kept, ak, pad_multiple=256)),
+        "gather_x_and_act": (2 * R * (d + wm) * 2 + (Rp - R) * (d + wm) * 2,
+                             lambda c: lemo.lemo_gather_pad_multi([xs[c], acts[c]], [xk, ak], b, kept, n_kept,
+                                                                  pad_multiple=256)),
+        "scatter": (3 * R * d * 2, lambda c: lemo.lemo_scatter_residual(res[c], b, kept, n_kept, y)),
+    }
+    all_kept = torch.arange(N // b, dtype=torch.int32, device=dev)
+    n_all = torch.tensor([N // b], dtype=torch.int32, device=dev)
+    xcopy = torch.empty_like(x)
+    calls["copy_ceiling"] = (2 * N * d * 2, lambda c: lemo.lemo_gather_pad(xs[c], b, all_kept, n_all, xcopy))
+    calls["torch_copy"] = (2 * N * d * 2, lambda c: xcopy.copy_(xs[c]))
+    out = {}
+    for name, (by, fn) in calls.items():
+        for c in range(6):
+            fn(c % 3)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for i in range(reps):
-            flush.sum()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        res[name] = float(np.median(ts))
-    return res
+            fn(i % 3)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = by / (ms * 1e-3) / 1e9
+        out[name] = {"bytes": int(by), "us": ms * 1e3, "GBps": gbps, "frac": gbps / PEAK_HBM_GBS}
+    del xs, acts, res, xcopy
+    return out
 
 
-def cpu_baseline(L, w):
-    """The oracle on the host cores, on a bounded sample of one step: exact
-    scores for `s` of the nb query blocks against every key block (scaled up by
-    nb / s), plus the full predictor, select, gather of X and of the MLP
-    activation, and scatter."""
+def chain_13b(stream, dev, reps=5):
+    """The Llama2-13B-shaped four-layer chain (N = 32768, d = 5120, blocks of
+    128, predictor rank 256) on one stream with no host synchronisation: per
+    layer, predicted scores of the current residual stream, top-k select
+    (keep 60 / 45 / 35 / 25 %), gather of the kept rows (the layer's input),
+    and in-place addition of a stand-in layer output.  Inputs are seeded
+    Gaussian tensors drawn on the device (the work does not depend on the
+    values: top-k fixes the kept count).  Per-layer stage times are mean
+    event times over `reps` chains; algorithmic bytes: the predictor reads X
+    once (plus its weights), the gather moves 2 R d 2 B, the scatter 3 R d 2 B;
+    the ideal time is the total at 8 TB/s."""
+    import torch
+    from contextual_token_sparsity_amd import lemo, synth
+    w = synth.WORKLOADS["llama2-13b-n32k-4layer"]
+    N, d, b, r = w.n_tokens, w.d_model, w.block, w.rank
+    nb = N // b
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    resid = torch.randn(N, d, device=dev, generator=g).to(torch.bfloat16)
+    layers = []
+    for _ in w.keep_pct:
+        wt = [(torch.randn(*s_, device=dev, generator=g) / s_[0] ** 0.5).to(torch.bfloat16)
+              for s_ in ((d, r), (r, r), (d, r), (r, r))]
+        yl = torch.randn(N, d, device=dev, generator=g).to(torch.bfloat16)
+        layers.append((wt, yl))
+    I = torch.empty(nb, dtype=torch.float32, device=dev)
+    ws = torch.empty(lemo.lemo_predict_scores_workspace(N, d, b, r), dtype=torch.uint8, device=dev)
+    mask = torch.empty(nb, dtype=torch.uint8, device=dev)
+    kept = torch.empty(nb, dtype=torch.int32, device=dev)
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    theta = torch.empty(1, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    xin = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    ks = [synth.keep_count(p, nb) for p in w.keep_pct]
+    ev = {}
+
+    def mark(key):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(key, []).append(e)
+
+    def chain(timed):
+        if timed:
+            mark("start")
+        for li, ((wt, yl), k) in enumerate(zip(layers, ks)):
+            lemo.lemo_predict_scores(resid, *wt, b, scores=I, workspace=ws)
+            if timed:
+                mark((li, "predict"))
+            lemo.lemo_select_mask(I, lemo.SELECT_TOPK, keep_blocks=k, mask=mask, kept_blocks=kept, n_kept=n_kept,
+                                  threshold_used=theta, dev_status=status)
+            if timed:
+                mark((li, "select"))
+            lemo.lemo_gather_pad(resid, b, kept, n_kept, xin, dev_status=status)
+            if timed:
+                mark((li, "gather"))
+            lemo.lemo_scatter_residual(resid, b, kept, n_kept, yl, dev_status=status)
+            if timed:
+                mark((li, "scatter"))
+
+    _settle(lambda: chain(False))
+    for _ in range(reps):
+        chain(True)
+    torch.cuda.synchronize()
+
+    def span(a, b_):
+        return float(np.mean([x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])]))
+
+    prev = "start"
+    layers_out = []
+    total_bytes = 0
+    weights_bytes = 2 * (2 * d * r + 2 * r * r)
+    for li, k in enumerate(ks):
+        R = k * b
+        by = {"predict": N * d * 2 + weights_bytes, "gather": 2 * R * d * 2, "scatter": 3 * R * d * 2}
+        t = {}
+        for st_ in ("predict", "select", "gather", "scatter"):
+            t[st_] = span(prev, (li, st_))
+            prev = (li, st_)
+        total_bytes += sum(by.values())
+        layers_out.append({
+            "keep_pct": w.keep_pct[li], "kept_blocks": k, "us": {kk: v * 1e3 for kk, v in t.items()},
+            "GBps": {kk: by[kk] / (t[kk] * 1e-3) / 1e9 for kk in by},
+            "frac": {kk: by[kk] / (t[kk] * 1e-3) / 1e9 / PEAK_HBM_GBS for kk in by}})
+    total_ms = span("start", (len(ks) - 1, "scatter"))
+    ideal_us = total_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
+    st = int(status.item())
+    del layers, resid, xin
+    return {"workload": "Llama2-13B-shaped, 4 layers: N=32768, d=5120, block 128, rank 256, top-k 60/45/35/25%",
+            "chain_us": total_ms * 1e3, "bytes": int(total_bytes), "ideal_us_at_8TBps": ideal_us,
+            "frac_of_ideal": ideal_us / (total_ms * 1e3), "token_layers_per_s": 4 * N / (total_ms * 1e-3),
+            "layers": layers_out, "dev_status": st}
+
+
+def select_topk(stream, dev):
+    """Latency of the top-k select (keep 30 %) at 256 and 8192 blocks on
+    seeded random scores: mean event time of 20 calls after a settle phase."""
+    import torch
+    from contextual_token_sparsity_amd import lemo, synth
+    out = {}
+    for nb in (256, 8192):
+        g = torch.Generator(device=dev).manual_seed(nb)
+        s_ = torch.rand(nb, device=dev, generator=g)
+        bufs = (torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+        k = synth.keep_count(30, nb)
+        t = _mean_ms(lambda: lemo.lemo_select_mask(s_, lemo.SELECT_TOPK, keep_blocks=k, mask=bufs[0],
+                                                   kept_blocks=bufs[1], n_kept=bufs[2], threshold_used=bufs[3]),
+                     stream, reps=20)
+        out[f"nb{nb}_us"] = t * 1e3
+    return out
+
+
+def cpu_baseline(L, w, full=False):
+    """The oracle on the host cores, timed per stage at the step's boundaries
+    on a bounded sample of one step: exact scores for `s` of the nb query
+    blocks against every key block (scaled up by nb / s; with `full`, all of
+    them once), then the full predictor, select, gather of X, gather of the
+    MLP activation and scatter.  Beside it, the whole exact-score oracle at
+    the two smaller exact configurations (1024 tokens: median of 3 runs;
+    OPT-1.3B at 4096 tokens: one run)."""
     from oracle import lemo_oracle as O
+    from contextual_token_sparsity_amd import synth
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     nb = w.n_blocks
-    s = 8
+    s = nb if full else 8
     print(f"[bench] cpu baseline: oracle on {s}/{nb} query blocks + full predictor/movement", file=sys.stderr,
           flush=True)
-    t = time.perf_counter()
-    O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER,
-                         query_blocks=list(range(0, nb, nb // s))[:s])
-    t_exact = (time.perf_counter() - t) * nb / s
-    t = time.perf_counter()
-    _, I_hat, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block)
-    _, kept, nk, _ = O.select_mask(I_hat.astype(np.float32), O.SELECT_MEAN)
+    stages = {}
+
+    def timed(name, fn, scale=1.0):
+        t = time.perf_counter()
+        r = fn()
+        stages[name] = (time.perf_counter() - t) * scale
+        return r
+
+    timed("exact_scores", lambda: O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER,
+                                                        query_blocks=list(range(0, nb, nb // s))[:s]),
+          nb / s)
+    _, I_hat, _, _ = timed("predict_scores", lambda: O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block))
+    _, kept, nk, _ = timed("select_mask", lambda: O.select_mask(I_hat.astype(np.float32), O.SELECT_MEAN))
     R = nk * w.block
     cap = -(-R // 256) * 256
-    O.gather_pad(L.x, w.block, kept, nk, np.zeros((cap, w.d_model), np.uint16), 256)
-    O.gather_pad(L.act, w.block, kept, nk, np.zeros((cap, w.mlp_width), np.uint16), 256)
-    O.scatter_residual(L.x, w.block, kept, nk, L.y[O.kept_token_rows(kept, nk, w.block)])
-    t_rest = time.perf_counter() - t
-    t_step = t_exact + t_rest
+    timed("gather_x", lambda: O.gather_pad(L.x, w.block, kept, nk, np.zeros((cap, w.d_model), np.uint16), 256))
+    timed("gather_act", lambda: O.gather_pad(L.act, w.block, kept, nk, np.zeros((cap, w.mlp_width), np.uint16), 256))
+    y = L.y[O.kept_token_rows(kept, nk, w.block)]
+    timed("scatter_residual", lambda: O.scatter_residual(L.x, w.block, kept, nk, y))
+    t_step = sum(stages.values())
+    small = {}
+    for name, runs in (("tiny", 3), ("opt1.3b-n4k", 1)):
+        sw = synth.WORKLOADS[name]
+        Ls = synth.make_layer(sw.n_tokens, sw.d_model, sw.block, sw.seed, n_heads=sw.n_heads,
+                              head_dim=sw.head_dim, planted_frac=sw.planted_frac, with_y=False)
+        ts = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            O.exact_block_scores(Ls.q, Ls.k, sw.n_heads, sw.head_dim, sw.block, O.REDUCE_PAPER)
+            ts.append(time.perf_counter() - t)
+        med = float(np.median(ts))
+        small[name] = {"exact_scores_s": med, "runs": runs, "tokens_per_s": sw.n_tokens / med}
     return {
         "value": w.n_tokens / t_step,
         "unit": "tokens/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"exact scores of {s} of {nb} query blocks (x{nb // s}) + full predictor, mean select, "
-                  f"gathers and scatter; est. step {t_step:.1f} s",
+        "sample": (f"exact scores of {s} of {nb} query blocks" + (f" (x{nb // s})" if s < nb else "") +
+                   f" + full predictor, mean select, gathers and scatter; est. step {t_step:.1f} s"),
+        "stages_s": stages,
+        "exact_scores_small_configs": small,
     }
 
 
