@@ -968,6 +968,51 @@ def test_pipeline_tiny(path):
         assert np.array_equal(host_bits(xd), ref_res)
 
 
+def test_headline_step_chain():
+    """The benchmark's step at the Llama2-7B N=16K shape, chained on the GPU
+    exactly as bench.py runs it (predicted scores -> MEAN select -> one
+    gather launch for X and the MLP activation, padded to 256 -> in-place
+    addition), against the oracle's own chain: scores within the tolerance,
+    the mask equal to the oracle's except on near-threshold blocks, and the
+    movement bit-exact against the oracle's movement on the GPU's kept list
+    (which is the oracle's list whenever the masks agree)."""
+    w = synth.WORKLOADS["llama2-7b-n16k"]
+    N, d, b, wm = w.n_tokens, w.d_model, w.block, w.mlp_width
+    say("headline step chain")
+    L = synth.make_layer(N, d, b, w.seed, rank=w.rank, mlp_width=wm, planted_frac=w.planted_frac)
+    _, I_ref, _, _ = O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, b)
+    mask_r, kept_r, nk_r, th_r = O.select_mask(I_ref.astype(np.float32), O.SELECT_MEAN)
+    xd, ad, yd = dev(L.x), dev(L.act), dev(L.y)
+    resd = xd.clone()
+    cap = N
+    xk = torch.empty((cap, d), dtype=torch.int16, device="cuda")
+    ak = torch.empty((cap, wm), dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    I, _ = lemo.lemo_predict_scores(xd, dev(L.u_q), dev(L.v_q), dev(L.u_k), dev(L.v_k), b)
+    mask, kept, nk, th = lemo.lemo_select_mask(I, lemo.SELECT_MEAN, dev_status=status)
+    lemo.lemo_gather_pad_multi([xd, ad], [xk, ak], b, kept, nk, pad_multiple=256, dev_status=status)
+    lemo.lemo_scatter_residual(resd, b, kept, nk, yd, dev_status=status)
+    torch.cuda.synchronize()
+    ok, worst = scores_close(I.cpu().numpy(), I_ref)
+    assert ok, worst
+    ok, diff = mask_acceptable(mask.cpu().numpy(), mask_r, I_ref, th_r)
+    assert ok, diff
+    assert abs(float(th.item()) - float(th_r)) <= 1e-2 * abs(float(th_r))
+    assert int(status.item()) == 0
+    nkg = int(nk.item())
+    kg = kept.cpu().numpy()[:nkg]
+    if diff.size == 0:
+        assert nkg == nk_r and np.array_equal(kg, kept_r)
+    else:
+        say("near-threshold mask difference on blocks", diff)
+    R = nkg * b
+    Rp = -(-R // 256) * 256
+    for src, dst, width in ((L.x, xk, d), (L.act, ak, wm)):
+        ref, _ = O.gather_pad(src, b, kg, nkg, np.zeros((Rp, width), np.uint16), 256)
+        assert np.array_equal(host_bits(dst)[:Rp], ref)
+    assert np.array_equal(host_bits(resd), O.scatter_residual(L.x, b, kg, nkg, L.y[:R]))
+
+
 def test_pipeline_13b_four_layer_chain():
     """Llama2-13B-shaped stack (N=32768, d=5120, block 128, rank 256), four
     layers chained on the GPU with no host round trip: predicted scores of the
