@@ -34,6 +34,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "llama2-7b-n16k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_scores_llama2-7b-n16k_traffic.json")
 CLOCK_SETTLE_S = 0.3
+SECTIONS = ("movement", "copy", "chain", "select", "causal", "headmax", "mlp", "recompute", "token", "fused",
+            "other_configs")
 
 
 def parse():
@@ -50,7 +52,18 @@ def parse():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the exact scores at the smaller configurations (they launch the same kernel "
                          "instantiation as the step, which would mix into a profiler's per-kernel average)")
-    return ap.parse_args()
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated supplementary sections to run after the step (default: all of "
+                         + ", ".join(SECTIONS) + "); profiled runs name only the ones they need so that each "
+                         "kernel's launches come from one call site")
+    args = ap.parse_args()
+    args.sections = [x for x in args.sections.split(",") if x]
+    unknown = set(args.sections) - set(SECTIONS)
+    if unknown:
+        ap.error(f"unknown sections {sorted(unknown)}")
+    if args.no_other_configs and "other_configs" in args.sections:
+        args.sections.remove("other_configs")
+    return args
 
 
 def load_traffic(causal=False):
@@ -227,16 +240,27 @@ def main():
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
     }
-    out["movement"] = movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev)
-    out["chain_13b"] = chain_13b(stream, dev)
-    out["select_topk"] = select_topk(stream, dev)
-    out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
-    out["other_head_reduce"] = other_head_reduce(q, k, N, H, hd, b, mode, stream, dev)
-    out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
-    out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
-    out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
-    out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
-    if not args.no_other_configs:
+    sec = args.sections
+    if "movement" in sec or "copy" in sec:
+        out["movement"] = movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev,
+                                             calls=("movement" in sec, "copy" in sec))
+    if "chain" in sec:
+        out["chain_13b"] = chain_13b(stream, dev)
+    if "select" in sec:
+        out["select_topk"] = select_topk(stream, dev)
+    if "causal" in sec:
+        out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
+    if "headmax" in sec:
+        out["other_head_reduce"] = other_head_reduce(q, k, N, H, hd, b, mode, stream, dev)
+    if "mlp" in sec:
+        out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
+    if "recompute" in sec:
+        out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
+    if "token" in sec:
+        out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
+    if "fused" in sec:
+        out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
+    if "other_configs" in sec:
         out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -470,7 +494,7 @@ def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):
     return res
 
 
-def movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev, reps=30):
+def movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev, reps=30, calls=(True, True)):
     """Each movement call on the step's mask, launched back to back `reps`
     times with the source rotated over three copies (so every launch reads
     data it last touched two launches earlier, more than the 256 MB Infinity
@@ -489,7 +513,8 @@ def movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev, re
     res = [x.clone() for _ in range(3)]
     xk = torch.empty((Rp, d), dtype=torch.int16, device=dev)
     ak = torch.empty((Rp, wm), dtype=torch.int16, device=dev)
-    calls = {
+    want_moves, want_copy = calls
+    calls = {} if not want_moves else {
         "gather_x": (2 * R * d * 2 + (Rp - R) * d * 2,
                      lambda c: lemo.lemo_gather_pad(xs[c], b, kept, n_kept, xk, pad_multiple=256)),
         "gather_act": (2 * R * wm * 2 + (Rp - R) * wm * 2,
@@ -502,8 +527,9 @@ def movement_streaming(x, act, y, kept, n_kept, nk, N, d, wm, b, stream, dev, re
     all_kept = torch.arange(N // b, dtype=torch.int32, device=dev)
     n_all = torch.tensor([N // b], dtype=torch.int32, device=dev)
     xcopy = torch.empty_like(x)
-    calls["copy_ceiling"] = (2 * N * d * 2, lambda c: lemo.lemo_gather_pad(xs[c], b, all_kept, n_all, xcopy))
-    calls["torch_copy"] = (2 * N * d * 2, lambda c: xcopy.copy_(xs[c]))
+    if want_copy:
+        calls["copy_ceiling"] = (2 * N * d * 2, lambda c: lemo.lemo_gather_pad(xs[c], b, all_kept, n_all, xcopy))
+        calls["torch_copy"] = (2 * N * d * 2, lambda c: xcopy.copy_(xs[c]))
     out = {}
     for name, (by, fn) in calls.items():
         for c in range(6):

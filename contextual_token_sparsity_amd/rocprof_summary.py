@@ -12,6 +12,10 @@
     # `bench.py` (SQ/GRBM/TCP counters listed in BUSY_PASSES)
     python -m contextual_token_sparsity_amd.rocprof_summary busy PASS1_CSV PASS2_CSV OUT_TXT "COMMANDS"
 
+    # HBM bytes per launch of the movement and pooling kernels, split by grid
+    # (two counter runs with --copy-probe, and a kernel trace of the same command)
+    python -m contextual_token_sparsity_amd.rocprof_summary movement FETCH_CSV WRITE_CSV TRACE_CSV OUT_TXT "COMMANDS"
+
 The traffic counters are calibrated on the plain 1 GiB device-to-device copy that
 `bench.py --copy-probe` issues: the ratio of its known bytes to what each
 counter reports scales the exact-score kernel's readings.
@@ -248,6 +252,69 @@ def busy(pass1_csv: str, pass2_csv: str, out_txt: str, commands: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+MOVEMENT_KERNELS = ("k_gather", "k_scatter", "k_pool")
+
+
+def _short(name: str) -> str:
+    for k in MOVEMENT_KERNELS:
+        if f"::{k}" in name or name.startswith(k):
+            return k + ("<sub>" if "k_scatter<true" in name else "")
+    return ""
+
+
+def _copy_scale(counter_csv: str) -> float:
+    """Bytes per counted KiB, from the largest copyBuffer dispatch (the 1 GiB copy probe)."""
+    best = 0.0
+    for r in csv.DictReader(open(counter_csv)):
+        if "copyBuffer" in r["Kernel_Name"]:
+            best = max(best, float(r["Counter_Value"]))
+    if not best:
+        raise SystemExit(f"no copy-probe dispatch in {counter_csv}")
+    return COPY_BYTES / best
+
+
+def _by_grid(counter_csv: str):
+    out = defaultdict(list)
+    for r in csv.DictReader(open(counter_csv)):
+        k = _short(r["Kernel_Name"])
+        if k:
+            out[(k, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return out
+
+
+def movement(fetch_csv: str, write_csv: str, trace_csv: str, out_txt: str, commands: str) -> None:
+    """Per launch of each movement / pooling kernel, grouped by grid size
+    (one group per call site in a run of bench.py that names only the
+    sections it needs): HBM bytes read and written (FETCH_SIZE, WRITE_SIZE,
+    each scaled by what it reads for the 1 GiB copy probe) and the median
+    kernel-trace duration, hence the HBM rate the counters imply."""
+    fs, ws = _copy_scale(fetch_csv), _copy_scale(write_csv)
+    f, w = _by_grid(fetch_csv), _by_grid(write_csv)
+    durs = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        k = _short(r["Kernel_Name"])
+        if k:
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            durs[(k, g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# HBM traffic of the movement and pooling kernels (rocprofv3 counters), by grid size",
+             f"# commands: {commands}", "",
+             f"copy probe scale: FETCH_SIZE x{fs / 1024:.3f} bytes per counted byte, "
+             f"WRITE_SIZE x{ws / 1024:.3f}", "",
+             f"{'kernel':<14} {'grid (work-items)':>18} {'launches':>8} {'read MB':>9} {'write MB':>9} "
+             f"{'med us':>8} {'GB/s':>8} {'of 8 TB/s':>9}"]
+    for key in sorted(set(f) | set(w)):
+        fv, wv = f.get(key, []), w.get(key, [])
+        rd = sum(fv) / len(fv) * fs if fv else float("nan")
+        wr = sum(wv) / len(wv) * ws if wv else float("nan")
+        dl = sorted(durs.get(key, []))
+        med = dl[len(dl) // 2] if dl else float("nan")
+        rate = (rd + wr) / (med * 1e-6) / 1e9 if dl else float("nan")
+        lines.append(f"{key[0]:<14} {key[1]:>18} {len(fv):>8} {rd / 1e6:>9.1f} {wr / 1e6:>9.1f} {med:>8.1f} "
+                     f"{rate:>8.0f} {rate / 8000:>9.1%}")
+    with open(out_txt, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1] if len(sys.argv) > 1 else ""
     if cmd == "trace" and len(sys.argv) in (5, 6):
@@ -256,6 +323,8 @@ if __name__ == "__main__":
         traffic(*sys.argv[2:7])
     elif cmd == "busy" and len(sys.argv) == 6:
         busy(*sys.argv[2:6])
+    elif cmd == "movement" and len(sys.argv) == 7:
+        movement(*sys.argv[2:7])
     else:
         print(__doc__)
         sys.exit(2)

@@ -103,3 +103,42 @@ def test_busy_needs_score_dispatches(tmp_path):
     write_counters(c1, [(1, "copyBuffer", 1, "GRBM_GUI_ACTIVE", 8, 0, 1)])
     with pytest.raises(SystemExit):
         R.busy(str(c1), str(c1), str(tmp_path / "o.txt"), "cmd")
+
+
+def test_movement_groups_by_grid(tmp_path):
+    """Movement kernels grouped by grid size: counter readings scaled by the
+    copy probe, durations from the kernel trace, the scatter's subtraction
+    variant kept apart."""
+    G = "(anonymous namespace)::k_gather((anonymous namespace)::GatherArgs, int, ...)"
+    S = "void (anonymous namespace)::k_scatter<false>(unsigned short*, int, ...)"
+    SUB = "void (anonymous namespace)::k_scatter<true>(unsigned short*, int, ...)"
+    fetch = [(1, "copyBuffer", 1, "FETCH_SIZE", 524288, 0, 1),
+             (2, G, 100, "FETCH_SIZE", 1000, 0, 1), (3, G, 100, "FETCH_SIZE", 3000, 0, 1),
+             (4, G, 200, "FETCH_SIZE", 500, 0, 1), (5, S, 100, "FETCH_SIZE", 7000, 0, 1),
+             (6, SUB, 100, "FETCH_SIZE", 9000, 0, 1), (7, "other_kernel", 100, "FETCH_SIZE", 1, 0, 1)]
+    write = [(1, "copyBuffer", 1, "WRITE_SIZE", 1048576, 0, 1),
+             (2, G, 100, "WRITE_SIZE", 4000, 0, 1), (3, G, 100, "WRITE_SIZE", 4000, 0, 1),
+             (4, G, 200, "WRITE_SIZE", 2000, 0, 1), (5, S, 100, "WRITE_SIZE", 3000, 0, 1),
+             (6, SUB, 100, "WRITE_SIZE", 3000, 0, 1)]
+    fc, wc, tc, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.csv", tmp_path / "o.txt"
+    write_counters(fc, fetch)
+    write_counters(wc, write)
+    with open(tc, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, gx, gy, t in ((G, 50, 2, 2000), (G, 50, 2, 4000), (G, 50, 2, 3000), (G, 200, 1, 1000),
+                                (S, 100, 1, 5000)):
+            w.writerow({"Kernel_Name": name, "Grid_Size_X": gx, "Grid_Size_Y": gy, "Grid_Size_Z": 1,
+                        "Start_Timestamp": 0, "End_Timestamp": t})
+    R.movement(str(fc), str(wc), str(tc), str(out), "cmd")
+    lines = open(out).read().splitlines()
+    row = lambda k, g: next(l for l in lines if l.split()[:2] == [k, str(g)])
+    # gather at grid 100: fetch avg 2000 KiB-units x 2048 B = 4.096 MB read; write 4000 x 1024 = 4.096 MB;
+    # median duration 3 us -> 8.192 MB / 3 us = 2731 GB/s
+    r = row("k_gather", 100).split()
+    assert r[2] == "2" and r[3] == "4.1" and r[4] == "4.1" and r[5] == "3.0" and r[6] == "2731"
+    assert row("k_gather", 200).split()[3] == "1.0"
+    assert row("k_scatter", 100).split()[3] == "14.3"
+    assert row("k_scatter<sub>", 100).split()[3] == "18.4"
+    assert not any(l.startswith("other_kernel") for l in lines)
