@@ -3,6 +3,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "lemo_internal.h"
@@ -57,7 +58,12 @@ lemo_status check_offsets(int rows, int ld, const char* name) {
 extern "C" {
 
 const char* lemo_status_string(lemo_status s) {
-  switch (s) {
+  // A C caller may pass any int here; reading an out-of-range value as the
+  // enum type is undefined in C++, so the code is taken from its bytes.
+  static_assert(sizeof(lemo_status) == sizeof(int), "lemo_status is an int-sized enum");
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case LEMO_OK: return "ok";
     case LEMO_ERR_INVALID_ARG: return "invalid argument";
     case LEMO_ERR_UNSUPPORTED: return "unsupported shape";

@@ -14,7 +14,9 @@ import re
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "liblemo.so")
+# LEMO_LIB_PATH selects another build of the same library (the CPU tests
+# point it at the sanitizer build of the host-side layer)
+LIB_PATH = os.environ.get("LEMO_LIB_PATH") or os.path.join(PKG, "liblemo.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "lemo.h")
 
 LEMO_OK = 0
