@@ -382,6 +382,7 @@ PRED_RAGGED = [
     (200, 128, 32, 32),
     (130, 512, 64, 128),
     (4000, 192, 256, 96),
+    (3001, 128, 2, 32),       # 1501 blocks, the last of one row: two key blocks per pair workgroup, one left over
 ]
 
 
@@ -485,6 +486,9 @@ PRED_SMALL = [
     (1024, 512, 64, 32),
     (2048, 192, 8, 96),
     (4096, 320, 256, 256),
+    (4096, 256, 2, 64),       # 2048 blocks: two key blocks per pair workgroup
+    (2048, 1280, 32, 32),     # five slices of d_model in the hidden product
+    (1024, 512, 8, 160),      # a rank above 128 that is not a power of two
 ]
 
 
