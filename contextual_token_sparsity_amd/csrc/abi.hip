@@ -275,9 +275,11 @@ lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model,
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
           "predictor matrices must be 16-byte aligned");
   const size_t need = lemo_token_ws_bytes(n_tokens, d_model, rank);
-  REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
-          "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
-  REQUIRE(aligned16(workspace), LEMO_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, LEMO_ERR_WORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    REQUIRE(aligned16(workspace), LEMO_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  }
   return device_status(lemo_launch_token_embed(x, n_tokens, d_model, ld_x, u_q, v_q, u_k, v_k, rank, q_hat, k_hat,
                                                ld_out, workspace, static_cast<hipStream_t>(stream)),
                        "lemo_token_embeddings launch");

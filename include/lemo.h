@@ -233,8 +233,11 @@ lemo_status lemo_predict_scores_noalloc(const lemo_bf16* x, int n_tokens, int d_
  *  x             bf16 [n_tokens][ld_x], d_model columns used (d_model % 64 == 0).
  *  u_q, u_k      bf16 [d_model][rank]; v_q, v_k bf16 [rank][rank] (rank % 64 == 0, <= 256).
  *  q_hat, k_hat  bf16 [n_tokens][ld_out] outputs, rank columns written.
- *  workspace     lemo_token_embeddings_workspace() bytes (transposed weights
- *                and the [n_tokens][2 rank] hidden activations).
+ *  workspace     lemo_token_embeddings_workspace() bytes.  Rank 128 with
+ *                d_model % 256 == 0 runs as one fused launch and needs none
+ *                (the function returns 0 and workspace may be NULL); other
+ *                shapes hold the transposed weights and the [n_tokens][2 rank]
+ *                hidden activations there.
  * Errors: INVALID_ARG, UNSUPPORTED (d_model, rank), ALIGNMENT, WORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t lemo_token_embeddings_workspace(int n_tokens, int d_model, int rank);

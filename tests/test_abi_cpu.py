@@ -121,7 +121,8 @@ def te(L, x=P, n=1024, d=512, ldx=512, uq=P, r=128, q=P, k=P, ldo=128, ws=P, wsb
     (dict(n=0), INVALID), (dict(r=0), INVALID), (dict(ldx=256), INVALID), (dict(ldo=64), INVALID),
     (dict(d=100, ldx=104), UNSUP), (dict(r=96, ldo=96), UNSUP), (dict(r=320, ldo=320), UNSUP),
     (dict(x=P2), ALIGN), (dict(uq=P2), ALIGN), (dict(q=P2), ALIGN), (dict(ldo=132), ALIGN),
-    (dict(ws=NULL), WS), (dict(wsb=1000), WS),
+    # rank 64 needs a workspace (rank 128 at d_model 512 runs fused, without one)
+    (dict(ws=NULL, r=64, ldo=64), WS), (dict(wsb=1000, r=64, ldo=64), WS), (dict(ws=P2, r=64, ldo=64), ALIGN),
 ])
 def test_token_embeddings_rejects(L, kw, status):
     assert te(L, **kw) == status
@@ -129,8 +130,12 @@ def test_token_embeddings_rejects(L, kw, status):
 
 
 def test_token_embeddings_workspace(L):
-    # [U_q | U_k]^T + V_q^T, V_k^T + hidden [N][2r], each 256-byte aligned
-    assert L.lemo_token_embeddings_workspace(16384, 4096, 128) == 256 * 4096 * 2 + 2 * 128 * 128 * 2 + 16384 * 256 * 2
+    # rank 128 with d_model % 256 == 0: the fused launch needs no workspace
+    assert L.lemo_token_embeddings_workspace(16384, 4096, 128) == 0
+    assert L.lemo_token_embeddings_workspace(32768, 5120, 128) == 0
+    # otherwise [U_q | U_k]^T + V_q^T, V_k^T + hidden [N][2r], each 256-byte aligned
+    assert L.lemo_token_embeddings_workspace(16384, 4096, 256) == 512 * 4096 * 2 + 2 * 256 * 256 * 2 + 16384 * 512 * 2
+    assert L.lemo_token_embeddings_workspace(16384, 4160, 128) == 256 * 4160 * 2 + 2 * 128 * 128 * 2 + 16384 * 256 * 2
     assert L.lemo_token_embeddings_workspace(0, 4096, 128) == 0
 
 

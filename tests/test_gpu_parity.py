@@ -1114,6 +1114,11 @@ TOKEN_SMALL = [
     (320, 192, 128),      # N not a multiple of the 128-row tile
     (200, 256, 256),      # rank 256: two column tiles per product
     (64, 64, 64),         # a single partial tile
+    # rank 128, d_model % 256 == 0: the fused one-launch path
+    (320, 256, 128),      # 2.5 row tiles, one round of four chunks
+    (64, 512, 128),       # a single partial row tile
+    (1000, 768, 128),     # 8 row tiles (query/key pairs on one XCD), ragged last tile
+    (2048, 1280, 128),    # 16 row tiles, 20 chunks
 ]
 
 
@@ -1139,6 +1144,25 @@ def test_token_embeddings_strided():
     out2 = padded(np.zeros((n, r), np.uint16), 72, 0x1234)
     lemo.lemo_token_embeddings(xp[:, :d], *[dev(a) for a in w], q_hat=out[:, :r], k_hat=out2[:, :r])
     ok, _ = _embeddings_close(host_bits(out)[:, :r], O.token_embeddings(x, w[0], w[1]))
+    assert ok
+    assert np.all(host_bits(out)[:, r:] == 0x1234) and np.all(host_bits(out2)[:, r:] == 0x1234)
+
+
+def test_token_embeddings_fused_strided_no_workspace():
+    """The fused path on row strides past the used columns, without a
+    workspace (it needs none)."""
+    n, d, r = 384, 256, 128
+    assert lemo.lemo_token_embeddings_workspace(n, d, r) == 0
+    x, w = _pred_inputs(29, n, d, r)
+    xp = padded(x, 304, 0x7FC0)
+    out = padded(np.zeros((n, r), np.uint16), 136, 0x1234)
+    out2 = padded(np.zeros((n, r), np.uint16), 136, 0x1234)
+    empty = torch.empty(0, dtype=torch.uint8, device="cuda")
+    lemo.lemo_token_embeddings(xp[:, :d], *[dev(a) for a in w], q_hat=out[:, :r], k_hat=out2[:, :r],
+                               workspace=empty)
+    ok, _ = _embeddings_close(host_bits(out)[:, :r], O.token_embeddings(x, w[0], w[1]))
+    assert ok
+    ok, _ = _embeddings_close(host_bits(out2)[:, :r], O.token_embeddings(x, w[2], w[3]))
     assert ok
     assert np.all(host_bits(out)[:, r:] == 0x1234) and np.all(host_bits(out2)[:, r:] == 0x1234)
 
