@@ -35,7 +35,7 @@ WORKLOAD = "llama2-7b-n16k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_scores_llama2-7b-n16k_traffic.json")
 CLOCK_SETTLE_S = 0.3
 SECTIONS = ("movement", "copy", "chain", "select", "causal", "headmax", "mlp", "recompute", "token", "fused",
-            "other_configs")
+            "other_configs", "gemm_ceiling")
 
 
 def parse():
@@ -262,6 +262,8 @@ def main():
         out["fused_movement"] = fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev)
     if "other_configs" in sec:
         out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
+    if "gemm_ceiling" in sec:
+        out["library_gemm_ceiling"] = library_gemm_ceiling(stream, dev)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -430,6 +432,33 @@ def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):
     return {"embeddings_ms": t_e, "scores_ms": t_s,
             "embeddings_TFLOPs": f_e / (t_e * 1e-3) / 1e12, "scores_TFLOPs": f_s / (t_s * 1e-3) / 1e12,
             "tokens_per_s": N / ((t_e + t_s) * 1e-3)}
+
+
+def library_gemm_ceiling(stream, dev, n=8192, reps=10):
+    """The vendor library's bf16 product (torch.mm, hipBLASLt) on random
+    normal operands at n x n x n: what a tuned dense kernel sustains on this
+    part once real data drives the matrix units and the clock settles under
+    that load (a reference point for the MFMA kernels' fractions, not part of
+    the path).  Mean event time over `reps` calls after a 0.3 s settle."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(321)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b_ = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    t = time.perf_counter()
+    while time.perf_counter() - t < CLOCK_SETTLE_S:
+        torch.mm(a, b_, out=c)
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.mm(a, b_, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": [n, n, n], "ms": ms, "TFLOPs": tf, "frac": tf / PEAK_BF16_TFLOPS}
 
 
 def fused_movement(x, resid, kept, n_kept, nk, N, d, b, stream, dev, reps=10):

@@ -25,7 +25,8 @@ namespace {
 // One thread owns 8 adjacent columns of one block and walks the block's rows
 // in order, so every column sum is formed in the same order as a sequential
 // loop.  64 threads cover 512 columns; the grid is (column groups, blocks).
-// X is read once, with streaming loads.
+// Plain loads: the gather of the kept rows that follows reads X again, and
+// finds part of it in the Infinity Cache.
 __global__ __launch_bounds__(64) void k_pool(const uint16_t* __restrict__ X, int ld, int d, int block,
                                              int n_tokens, float inv_block, uint16_t* __restrict__ xbar) {
   const int m = blockIdx.y;
@@ -37,9 +38,9 @@ __global__ __launch_bounds__(64) void k_pool(const uint16_t* __restrict__ X, int
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-#pragma unroll 4
+#pragma unroll 8
   for (int i = 0; i < rows; ++i) {
-    const uint4 v = lemo_load_stream(p + (size_t)i * ld);
+    const uint4 v = *reinterpret_cast<const uint4*>(p + (size_t)i * ld);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
