@@ -1119,6 +1119,7 @@ TOKEN_SMALL = [
     (64, 512, 128),       # a single partial row tile
     (1000, 768, 128),     # 8 row tiles (query/key pairs on one XCD), ragged last tile
     (2048, 1280, 128),    # 16 row tiles, 20 chunks
+    (4096, 5120, 128),    # the 13B model width: 80 chunks, 32 row tiles
 ]
 
 
