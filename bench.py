@@ -130,24 +130,26 @@ def main():
         e.record(stream)
         ev.setdefault(name, []).append(e)
 
-    def step(timed):
-        if timed:
-            mark("scores0")
+    # marks: 0 none, 1 around the exact scores only (the timed steps: the
+    # roofline's launch duration), 2 after every stage (the stage breakdown)
+    def step(marks):
+        if marks:
+            mark("scores0" if marks == 1 else "s_scores0")
         lemo.lemo_block_scores(q, k, H, hd, b, mode, scores=I_exact, workspace=ws_exact)
-        if timed:
-            mark("scores1")
+        if marks:
+            mark("scores1" if marks == 1 else "scores1_staged")
         lemo.lemo_predict_scores(x, uq, vq, uk, vk, b, scores=I_pred, workspace=ws_pred)
-        if timed:
+        if marks == 2:
             mark("predict1")
         lemo.lemo_select_mask(I_pred, lemo.SELECT_MEAN, mask=mask, kept_blocks=kept, n_kept=n_kept,
                               threshold_used=theta, dev_status=status)
-        if timed:
+        if marks == 2:
             mark("select1")
         lemo.lemo_gather_pad_multi([x, act], [xk, ak], b, kept, n_kept, pad_multiple=256, dev_status=status)
-        if timed:
+        if marks == 2:
             mark("gather1")
         lemo.lemo_scatter_residual(resid, b, kept, n_kept, y, dev_status=status)
-        if timed:
+        if marks == 2:
             mark("scatter1")
 
     # The GPU clock ramps up under sustained load; run untimed steps for at
@@ -156,11 +158,11 @@ def main():
     t_settle = time.perf_counter()
     settle_steps = 0
     while time.perf_counter() - t_settle < CLOCK_SETTLE_S:
-        step(False)
+        step(0)
         torch.cuda.synchronize()
         settle_steps += 1
     for _ in range(args.warmup):
-        step(False)
+        step(0)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -168,19 +170,25 @@ def main():
     t0.record(stream)
     host0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step(1)
     t1.record(stream)
     torch.cuda.synchronize()
     host_s = time.perf_counter() - host0
     total_ms = t0.elapsed_time(t1)
     ms_step = total_ms / args.steps
+    # the other stages' times from a second pass of the same number of steps
+    # with an event between stages (kept out of the timed steps above: each
+    # event record adds a small gap to the stream)
+    for _ in range(args.steps):
+        step(2)
+    torch.cuda.synchronize()
 
     def avg(a, b_):
         return float(np.mean([x.elapsed_time(y_) for x, y_ in zip(ev[a], ev[b_])]))
 
     stages = {
         "block_scores": avg("scores0", "scores1"),
-        "predict_scores": avg("scores1", "predict1"),
+        "predict_scores": avg("scores1_staged", "predict1"),
         "select_mask": avg("predict1", "select1"),
         "gather_pad_x_and_act": avg("select1", "gather1"),
         "scatter_residual": avg("gather1", "scatter1"),
@@ -585,8 +593,10 @@ def chain_13b(stream, dev, reps=5):
     (keep 60 / 45 / 35 / 25 %), gather of the kept rows (the layer's input),
     and in-place addition of a stand-in layer output.  Inputs are seeded
     Gaussian tensors drawn on the device (the work does not depend on the
-    values: top-k fixes the kept count).  Per-layer stage times are mean
-    event times over `reps` chains; algorithmic bytes: the predictor reads X
+    values: top-k fixes the kept count).  The chain time is the event time of
+    `reps` chains without events between stages; per-layer stage times are
+    mean event times over `reps` further chains with an event after each stage
+    (`chain_us_with_stage_events` is their sum); algorithmic bytes: the predictor reads X
     once (plus its weights), the gather moves 2 R d 2 B, the scatter 3 R d 2 B;
     the ideal time is the total at 8 TB/s."""
     import torch
@@ -637,9 +647,18 @@ def chain_13b(stream, dev, reps=5):
                 mark((li, "scatter"))
 
     _settle(lambda: chain(False))
+    # the whole chain without events between its stages, then the same number
+    # of chains with them for the per-stage times
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(reps):
+        chain(False)
+    c1.record(stream)
     for _ in range(reps):
         chain(True)
     torch.cuda.synchronize()
+    chain_ms = c0.elapsed_time(c1) / reps
 
     def span(a, b_):
         return float(np.mean([x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])]))
@@ -660,14 +679,14 @@ def chain_13b(stream, dev, reps=5):
             "keep_pct": w.keep_pct[li], "kept_blocks": k, "us": {kk: v * 1e3 for kk, v in t.items()},
             "GBps": {kk: by[kk] / (t[kk] * 1e-3) / 1e9 for kk in by},
             "frac": {kk: by[kk] / (t[kk] * 1e-3) / 1e9 / PEAK_HBM_GBS for kk in by}})
-    total_ms = span("start", (len(ks) - 1, "scatter"))
+    staged_ms = span("start", (len(ks) - 1, "scatter"))
     ideal_us = total_bytes / (PEAK_HBM_GBS * 1e9) * 1e6
     st = int(status.item())
     del layers, resid, xin
     return {"workload": "Llama2-13B-shaped, 4 layers: N=32768, d=5120, block 128, rank 256, top-k 60/45/35/25%",
-            "chain_us": total_ms * 1e3, "bytes": int(total_bytes), "ideal_us_at_8TBps": ideal_us,
-            "frac_of_ideal": ideal_us / (total_ms * 1e3), "token_layers_per_s": 4 * N / (total_ms * 1e-3),
-            "layers": layers_out, "dev_status": st}
+            "chain_us": chain_ms * 1e3, "chain_us_with_stage_events": staged_ms * 1e3, "bytes": int(total_bytes),
+            "ideal_us_at_8TBps": ideal_us, "frac_of_ideal": ideal_us / (chain_ms * 1e3),
+            "token_layers_per_s": 4 * N / (chain_ms * 1e-3), "layers": layers_out, "dev_status": st}
 
 
 def select_topk(stream, dev):

@@ -47,8 +47,9 @@ def _score_launches(trace_csv: str, timed_steps: int):
     """Per-dispatch durations (us) of the benchmark's exact-score launches,
     in dispatch order, from the kernel-trace CSV.  Only dispatches of at
     least half the longest one count (a much smaller launch of the same
-    instantiation would otherwise dilute the average).  The bench times
-    `timed_steps` steps right before its first causal launch."""
+    instantiation would otherwise dilute the average).  The bench runs its
+    `timed_steps` timed steps, then as many steps again with an event after
+    every stage (the stage breakdown), right before its first causal launch."""
     rows = list(csv.DictReader(open(trace_csv)))
     seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
     full = [(s, (e - s) / 1e3) for s, e, n in seq if SCORE_KERNEL in n]
@@ -58,12 +59,14 @@ def _score_launches(trace_csv: str, timed_steps: int):
     top = max(d for _, d in full)
     many = [(s, d) for s, d in full if d >= 0.5 * top]
     first_causal = causal[0][0] if causal else None
-    timed = [d for s, d in many if first_causal is None or s < first_causal][-timed_steps:]
+    before = [d for s, d in many if first_causal is None or s < first_causal]
+    timed = before[-2 * timed_steps:-timed_steps] if len(before) >= 2 * timed_steps else []
+    staged = before[-timed_steps:]
     lines = ["", f"{SCORE_KERNEL}, 32-head launches only ({len(full) - len(many)} much smaller launches left "
              f"out): {len(many)} launches, avg {sum(d for _, d in many) / len(many):.1f} us "
              "(includes the clock-settle launches)",
-             f"  the {len(timed)} launches just before the first causal launch (the bench's timed steps): "
-             f"avg {sum(timed) / max(len(timed), 1):.1f} us"]
+             f"  the bench's {len(timed)} timed steps: avg {sum(timed) / max(len(timed), 1):.1f} us; the "
+             f"{len(staged)} steps of the stage breakdown after them: avg {sum(staged) / max(len(staged), 1):.1f} us"]
     if causal:
         ds = [d for _, d in causal]
         lines.append(f"{CAUSAL_KERNEL}: {len(ds)} launches, avg {sum(ds) / len(ds):.1f} us; "

@@ -142,3 +142,32 @@ def test_movement_groups_by_grid(tmp_path):
     assert row("k_scatter", 100).split()[3] == "14.3"
     assert row("k_scatter<sub>", 100).split()[3] == "18.4"
     assert not any(l.startswith("other_kernel") for l in lines)
+
+
+def test_trace_separates_timed_and_staged_score_launches(tmp_path):
+    """Kernel-trace summary: the exact-score launches of the bench's timed steps
+    and of the stage-breakdown steps after them are averaged apart, both taken
+    right before the first causal launch; much smaller launches of the same
+    instantiation are left out."""
+    stats = tmp_path / "trace_kernel_stats.csv"
+    trace_csv = tmp_path / "trace_kernel_trace.csv"
+    out = tmp_path / "o.txt"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": SCORE, "Calls": 9, "AverageNs": 1, "MinNs": 1, "MaxNs": 1, "Percentage": 1})
+    # (start, duration ns, kernel): 3 settle launches, 2 timed, 2 staged, a small
+    # one-head launch of the same instantiation, then the causal launch and
+    # another full launch after it
+    seq = [(0, 5000, SCORE), (10, 5000, SCORE), (20, 5000, SCORE), (30, 4000, SCORE), (40, 6000, SCORE),
+           (50, 100, SCORE), (60, 5000, SCORE), (70, 7000, SCORE), (80, 7000, CAUSAL), (90, 5000, SCORE)]
+    with open(trace_csv, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for s, d, n in seq:
+            w.writerow({"Kernel_Name": n, "Start_Timestamp": s * 1000, "End_Timestamp": s * 1000 + d})
+    R.trace(str(stats), str(out), "cmd", 2)
+    text = open(out).read()
+    assert "1 much smaller launches left out" in text
+    assert "the bench's 2 timed steps: avg 5.0 us" in text          # 4000 and 6000 ns
+    assert "the 2 steps of the stage breakdown after them: avg 6.0 us" in text   # 5000 and 7000 ns
