@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "llama2-7b-n16k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_scores_llama2-7b-n16k_traffic.json")
 CLOCK_SETTLE_S = 0.3
-SECTIONS = ("movement", "copy", "chain", "select", "causal", "headmax", "mlp", "recompute", "token", "fused",
+SECTIONS = ("c4", "movement", "copy", "chain", "select", "causal", "headmax", "mlp", "recompute", "token", "fused",
             "other_configs", "gemm_ceiling")
 
 
@@ -244,6 +244,8 @@ def main():
                                  "GBps": (bytes_gx + bytes_ga) / (warm_ms["gather_x_and_act"] * 1e-3) / 1e9},
             "scatter": {"bytes": bytes_sc, "GBps": bytes_sc / (warm_ms["scatter"] * 1e-3) / 1e9}},
         "predictor_path_tokens_per_s": N / (sum(v for kk, v in stages.items() if kk != "block_scores") * 1e-3),
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
         "dev_status": st,
         "host_wall_s": host_s,
         "clock_settle_steps": settle_steps,
@@ -264,6 +266,10 @@ def main():
         out["mlp_scores"] = mlp_scores(act, N, wm, b, stream, dev)
     if "recompute" in sec:
         out["residual_recompute"] = recompute(resid, y, kept, n_kept, nk, d, b, stream)
+    if "c4" in sec:
+        out["c4_predictor_path"] = c4_predictor_path(
+            x, act, (uq, vq, uk, vk), resid, y, (xk, ak), (I_pred, ws_pred, mask, kept, n_kept, theta, status),
+            N, b, stream, dev)
     if "token" in sec:
         out["token_predictor"] = token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev)
     if "fused" in sec:
@@ -406,6 +412,58 @@ def recompute(resid, y, kept, n_kept, nk, d, b, stream):
     t = _mean_ms(lambda: lemo.lemo_residual_recompute(resid, b, kept, n_kept, y), stream)
     by = 3.0 * nk * b * d * 2
     return {"ms": t, "GBps": by / (t * 1e-3) / 1e9, "frac": by / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def c4_predictor_path(x, act, wts, resid, y, outs, bufs, N, b, stream, dev, iters=100, warm=10):
+    """The online layer the predictor drives (predicted scores -> MEAN select
+    -> gather of X and of the MLP activation in one launch -> in-place
+    addition), timed as one event pair around the whole sequence with no host
+    synchronisation inside, per iteration: `warm` untimed iterations, then
+    `iters` timed ones; median and minimum.  "warm": back to back; "cold": the
+    256 MB Infinity Cache is flushed before each iteration by writing a
+    512 MiB scratch buffer (outside the event pair).  Also without the
+    MLP-activation gather (X only).  tokens/s = N / time."""
+    import torch
+    from contextual_token_sparsity_amd import lemo
+    uq, vq, uk, vk = wts
+    xk, ak = outs
+    I_pred, ws_pred, mask, kept, n_kept, theta, status = bufs
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def seq(with_act):
+        lemo.lemo_predict_scores(x, uq, vq, uk, vk, b, scores=I_pred, workspace=ws_pred)
+        lemo.lemo_select_mask(I_pred, lemo.SELECT_MEAN, mask=mask, kept_blocks=kept, n_kept=n_kept,
+                              threshold_used=theta, dev_status=status)
+        if with_act:
+            lemo.lemo_gather_pad_multi([x, act], [xk, ak], b, kept, n_kept, pad_multiple=256, dev_status=status)
+        else:
+            lemo.lemo_gather_pad(x, b, kept, n_kept, xk, pad_multiple=256, dev_status=status)
+        lemo.lemo_scatter_residual(resid, b, kept, n_kept, y, dev_status=status)
+
+    res = {"iters": iters}
+    for with_act in (True, False):
+        for cold in (False, True):
+            for _ in range(warm):
+                if cold:
+                    scratch.zero_()
+                seq(with_act)
+            evs = []
+            for _ in range(iters):
+                if cold:
+                    scratch.zero_()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                seq(with_act)
+                e1.record(stream)
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b_) for a, b_ in evs]) * 1e3      # us
+            key = ("with" if with_act else "without") + "_mlp_gather_" + ("cold" if cold else "warm")
+            res[key] = {"median_us": float(np.median(t)), "min_us": float(t.min()),
+                        "tokens_per_s_median": N / (float(np.median(t)) * 1e-6)}
+    del scratch
+    return res
 
 
 def token_predictor(x, uq, vq, uk, vk, N, d, b, r, stream, dev, reps=10):
