@@ -769,9 +769,9 @@ def select_topk(stream, dev):
 def cpu_baseline(L, w, full=False):
     """The oracle on the host cores, timed per stage at the step's boundaries
     on a bounded sample of one step: exact scores for `s` of the nb query
-    blocks against every key block (scaled up by nb / s; with `full`, all of
-    them once), then the full predictor, select, gather of X, gather of the
-    MLP activation and scatter.  Beside it, the whole exact-score oracle at
+    blocks against every key block (one run, scaled up by nb / s; with
+    `full`, all of them once), then the full predictor, select, gather of X,
+    gather of the MLP activation and scatter (median of 3 runs each).  Beside it, the whole exact-score oracle at
     the two smaller exact configurations (1024 tokens: median of 3 runs;
     OPT-1.3B at 4096 tokens: one run)."""
     from oracle import lemo_oracle as O
@@ -787,15 +787,18 @@ def cpu_baseline(L, w, full=False):
           flush=True)
     stages = {}
 
-    def timed(name, fn, scale=1.0):
-        t = time.perf_counter()
-        r = fn()
-        stages[name] = (time.perf_counter() - t) * scale
+    def timed(name, fn, scale=1.0, runs=3):
+        ts = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t)
+        stages[name] = float(np.median(ts)) * scale
         return r
 
     timed("exact_scores", lambda: O.exact_block_scores(L.q, L.k, w.n_heads, w.head_dim, w.block, O.REDUCE_PAPER,
                                                         query_blocks=list(range(0, nb, nb // s))[:s]),
-          nb / s)
+          nb / s, runs=1)
     _, I_hat, _, _ = timed("predict_scores", lambda: O.predict_scores(L.x, L.u_q, L.v_q, L.u_k, L.v_k, w.block))
     _, kept, nk, _ = timed("select_mask", lambda: O.select_mask(I_hat.astype(np.float32), O.SELECT_MEAN))
     R = nk * w.block
