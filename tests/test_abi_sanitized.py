@@ -11,9 +11,21 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _stale(lib):
+    """True when the built library is missing or older than a source it is
+    built from (the HIP sources, their headers, the C-ABI header)."""
+    from contextual_token_sparsity_amd import build
+    if not os.path.exists(lib):
+        return True
+    srcs = [os.path.join(build.CSRC, f) for f in os.listdir(build.CSRC)]
+    srcs += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    built = os.path.getmtime(lib)
+    return any(os.path.getmtime(f) > built for f in srcs)
+
+
 def test_abi_tests_pass_under_asan_and_ubsan():
     from contextual_token_sparsity_amd import build
-    if not os.path.exists(build.HOSTCHECK_LIB):
+    if _stale(build.HOSTCHECK_LIB):
         build.build_host_check()
     env = dict(os.environ)
     env.update({
