@@ -278,6 +278,8 @@ def main():
         out["exact_scores_other_configs"] = exact_scores_other_configs(mode, stream, dev)
     if "gemm_ceiling" in sec:
         out["library_gemm_ceiling"] = library_gemm_ceiling(stream, dev)
+        # the exact-score kernel's rate against the vendor GEMM's on the same box
+        out["block_scores_vs_library_gemm"] = achieved / out["library_gemm_ceiling"]["TFLOPs"]
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
