@@ -47,6 +47,11 @@ EXACT_SMALL = [
     (96, 1, 64, 32),      # smaller than one tile
     (64, 1, 128, 64),     # a single block: only diagonal pairs to exclude
     (1024, 5, 128, 64),
+    # head_dim 64 with several heads (PAPER runs its chain from the running
+    # sum there, two heads per loop turn): 32-row blocks, and an odd head
+    # count with 128-row blocks
+    (256, 4, 64, 32),
+    (384, 3, 64, 128),
 ]
 
 
@@ -214,6 +219,7 @@ BATCHED_SMALL = [
     (1, 65, 2, 64, 64),       # a last block of one token
     (2, 1536, 4, 128, 64),    # 78 causal tiles: not a multiple of 8 (no XCD split)
     (1, 2048, 4, 128, 64),    # 136 causal tiles: XCD split, groups of 8 query tiles
+    (2, 200, 5, 64, 32),      # head_dim 64, an odd head count, ragged 32-row blocks
 ]
 
 
