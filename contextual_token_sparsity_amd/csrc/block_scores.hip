@@ -24,13 +24,15 @@
 //           from 0 and the head is folded in as sum += max(0, S^h).  For a
 //           non-negative float the bit pattern orders like a signed integer
 //           while a negative float is a negative integer, so the clamp is one
-//           v_max_i32 against 0.  At head_dim 64 the chain starts from the
-//           running sum instead and the fold is sum = max(sum + S^h, sum), one
-//           VALU op less (the two register sets swap roles from head to head,
-//           and the first MFMA of a head is written out so that its source
-//           is kept without a copy): 8-9 % faster there.  At head_dim 128 the
-//           same form is 5-7 % slower (each head's first MFMAs then wait for
-//           the fold), so that path keeps the chain from 0.
+//           v_max_i32 against 0.  At head_dim 64 (one chunk per head, so the
+//           fold weighs twice as much per MFMA) the chain starts from the
+//           running sum instead: it ends at sum + S^h, and the fold
+//           max(sum + S^h, sum) is one v_max_i32 per element.  The two
+//           register sets swap roles from head to head, and a head's fold is
+//           deferred to the next head's first k-step, one sub-tile ahead of
+//           each first MFMA, so that it runs under the MFMAs: 11 % faster
+//           there; at head_dim 128 within +-1 % (box-dependent), so that path
+//           keeps the chain from 0.
 //   HEADMAX (per-head block max): the head's accumulators are reduced with
 //           v_max_i32 starting from 0, which yields max(0, block max) (the
 //           clamp is free for the same reason), then across lanes; the clamped
@@ -176,10 +178,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     int ldk, long long bsq, long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr int kCPH = HD / kChunk;                      // chunks per head
-  // PAPER at head_dim 64 (one chunk per head, so the fold weighs twice as much
-  // per MFMA) starts each head's chain from the running sum: one VALU op per
-  // element instead of two.  At head_dim 128 that serialises each head's first
-  // MFMAs behind the fold and was measured 5-7 % slower, so it stays there.
+  // PAPER at head_dim 64 starts each head's MFMA chain from the running sum,
+  // so the fold is one max per element; the fold of a head is deferred to the
+  // next head's first k-step and interleaved one sub-tile at a time with its
+  // first MFMAs.  At head_dim 128 this measured within +-1 % of the chain
+  // from 0 (box-dependent), which stays there.
   constexpr bool kSumChain = MODE == 0 && HD == 64;
   constexpr int kParts = (MODE == 1 && BLK == 128) ? kMaxHeadsHeadmax : 1;
   __shared__ float part[kWaves][kParts];                 // HEADMAX, 128-row blocks: per-head wave maxima
@@ -291,6 +294,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum[a][b][e] = 0.f;
+  if (kSumChain) {   // the first head's deferred fold then reads zeros
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[0][a][b][e] = 0.f;
+  }
   float total[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // HEADMAX, blocks <= 64 rows: sum over heads
   int hm_lane = 0;                                // HEADMAX, blocks >= 64: this lane's running block max
 
@@ -362,18 +373,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             if (kSumChain) {
-              // PAPER at head_dim 64: even heads run their chain in acc[0]
-              // from the running sum in sum[], odd heads in sum[] from acc[0].
-              // The first MFMA keeps its source registers (the running sum
-              // is read again by the fold), written out because the compiler
-              // would otherwise copy them into the destination first; the
-              // s_nop covers the wait after the fold's VALU writes of them.
+              // PAPER: even heads run their chain in acc[0] from the running
+              // sum in sum[], odd heads in sum[] from acc[0].  At a head's
+              // first k-step, sub-tile by sub-tile: the previous head's fold
+              // (its chain c0 := max(c0, d), d holding the sum before that
+              // head), then the first MFMA, written out with its own
+              // destination because the compiler would otherwise copy the
+              // source into it first; the s_nop covers the wait after the
+              // fold's VALU writes of that source.
               lemo_f32x16& d = P == 0 ? acc[0][a][b] : sum[a][b];
-              const lemo_f32x16& c0 = P == 0 ? sum[a][b] : acc[0][a][b];
-              if (kc == 0 && s == 0)
+              lemo_f32x16& c0 = P == 0 ? sum[a][b] : acc[0][a][b];
+              if (kc == 0 && s == 0) {
+                // the previous head's fold of this sub-tile: c0 (its chain)
+                // = max(c0, d) (d still holds the sum before that head)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) c0[e] = __int_as_float(imax(__float_as_int(c0[e]), __float_as_int(d[e])));
                 asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
                              : "=&v"(d) : "v"(fa[cur][a]), "v"(fb[cur][b]), "v"(c0));
-              else
+                __builtin_amdgcn_sched_barrier(0);   // the next sub-tile's fold runs under this MFMA
+              } else
                 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], d, 0, 0, 0);
             } else if (kc == 0 && s == 0) {  // first k-step of a head: the chain starts from 0
               acc[P][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][a], fb[cur][b], lemo_f32x16{}, 0, 0, 0);
@@ -385,29 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // HEADMAX: excluded pairs leave the head's tile before it is folded in
-    // (one pass, only in waves that hold such pairs, outside the
-    // interleaved fold so the common path keeps its schedule)
-    if (MODE == 1 && mask_wave) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) exclude(acc[P][a][b], a, b);
-    }
-    if (kSumChain) {
-      // the chain holds sum + S^h, so sum + max(0, S^h) = max(sum + S^h, sum):
-      // one v_max per element (as integers: sum >= 0, and a negative float is
-      // a negative integer); the new sum stays in the chain's registers
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          lemo_f32x16& d = P == 0 ? acc[0][a][b] : sum[a][b];
-          const lemo_f32x16& prev = P == 0 ? sum[a][b] : acc[0][a][b];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) d[e] = __int_as_float(imax(__float_as_int(d[e]), __float_as_int(prev[e])));
-        }
-    } else if (MODE == 0) {
+    if (MODE == 0 && !kSumChain) {
       // sum += max(0, S^h): a negative float is a negative integer, so the
       // clamp is one v_max_i32 against 0
 #pragma unroll
@@ -418,6 +414,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
           for (int e = 0; e < 16; ++e)
             sum[a][b][e] += __int_as_float(imax(__float_as_int(acc[P][a][b][e]), 0));
     }
+    // HEADMAX: excluded pairs leave the head's tile before it is folded in
+    // (one pass, only in waves that hold such pairs, outside the
+    // interleaved fold so the common path keeps its schedule)
+    if (MODE == 1 && mask_wave) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) exclude(acc[P][a][b], a, b);
+    }
   };
 
   if (kSumChain) {
@@ -426,12 +431,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
       do_head(std::integral_constant<int, 0>{}, h);
       do_head(std::integral_constant<int, 1>{}, h + 1);
     }
-    if (h < n_heads) {   // an odd head count: the last head leaves the sum in acc[0]
+    if (h < n_heads) {   // an odd head count: the last head's chain is in acc[0]
       do_head(std::integral_constant<int, 0>{}, h);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) sum[a][b] = acc[0][a][b];
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            sum[a][b][e] = __int_as_float(imax(__float_as_int(acc[0][a][b][e]), __float_as_int(sum[a][b][e])));
+    } else {             // an even head count: the last head's chain is in sum
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            sum[a][b][e] = __int_as_float(imax(__float_as_int(sum[a][b][e]), __float_as_int(acc[0][a][b][e])));
     }
   } else if (MODE == 0) {
     for (int h = 0; h < n_heads; ++h) do_head(std::integral_constant<int, 0>{}, h);
