@@ -48,6 +48,12 @@
 // value; every step is positively homogeneous so this is exact up to
 // rounding.
 //
+// Full launches (no causal mask, whole blocks) with an even head count and
+// enough tiles to fill the chip run k_block_scores_pp instead: one
+// eight-wave workgroup per CU on a 256 x 128 tile, whose two groups of four
+// waves take turns between matrix phases and memory phases (its comment
+// below gives the schedule).
+//
 // Causal launches cover only the tiles on or below the tile diagonal; each
 // tile below it also writes the zeros of its mirror tile above.  A batch of
 // independent sequences is the grid's y dimension.  The column aggregate is a
@@ -543,6 +549,419 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave form of the same reduction (the launcher's choice for full,
+// unmasked launches with an even head count and enough tiles to fill the
+// chip).  One workgroup per CU owns a 256 x 128 tile (query rows x key
+// rows): 25 % fewer refill bytes per MFMA than two 128 x 128 workgroups.
+// Its waves form two groups of four, one wave of each group per SIMD, each
+// group a 2 x 2 grid of 64 x 64 wave tiles (group g: query rows 128 g ..
+// 128 g + 127).  The groups take turns between barriers: while one group
+// runs a whole 64-wide chunk of MFMAs from operands already in registers,
+// the other reads its next chunk's operands from LDS and folds its last head,
+// so every phase keeps the matrix cores of all four SIMDs busy with one
+// wave's MFMAs while the other wave's LDS reads and VALU work run beside
+// them.  The refills (direct global->LDS loads into a 3-stage ring of 48 KiB
+// stages) are issued by the multiplying group, one after every second MFMA.
+//
+// Phases: 2c (group 0 multiplies chunk c, group 1 reads it) and 2c+1
+// (group 1 multiplies chunk c, group 0 reads chunk c+1).  Chunk c+1 must be
+// in LDS at the barrier that ends phase 2c; each wave then has the loads of
+// chunks c+1 and c+2 in flight (group 1 issues its part of chunk c+3 in
+// phase 2c+1, group 0 its part of chunk c+2 in phase 2c), so the wait is
+// always "6 loads may remain".  Past the last chunk the loads repeat the last
+// chunk's columns into the stage that chunk number maps to, which is no
+// longer read, so the count holds to the end.  The stage of chunk c is free
+// once both groups have read it (phases 2c-1 and 2c).
+//
+// PAPER folds each head with one VALU op per element: head h runs its MFMA
+// chain in register set h % 2 starting from the other set, which holds the
+// running sum R, so the chain ends at R + S^h and the fold is
+// set[h % 2] = max(set[h % 2], set[1 - h % 2]) = R + max(0, S^h).  The first
+// MFMA of a head is written out in assembly with its own destination (the
+// compiler would otherwise copy the source set into it first).  HEADMAX
+// chains start from 0 and fold as in k_block_scores.
+namespace pp {
+constexpr int kTQ = 256, kTK = 128, kWaves = 8, kThreads = 512;
+constexpr int kStageQ = kTQ * kRowBytes;                 // 32 KiB
+constexpr int kStageK = kTK * kRowBytes;                 // 16 KiB
+constexpr int kStageBytes = kStageQ + kStageK;           // 48 KiB
+constexpr int kStages = 3;                               // 144 KiB
+constexpr int kDmaQ = kStageQ / (kThreads * 16);         // 4 loads of 16 B per lane
+constexpr int kDmaK = kStageK / (kThreads * 16);         // 2
+constexpr int kDma = kDmaQ + kDmaK;
+static_assert(kDmaQ * kThreads * 16 == kStageQ && kDmaK * kThreads * 16 == kStageK, "stage split");
+static_assert(kDma == 6, "the barrier waits count 6 loads per chunk and wave");
+
+// as tile_of, with 32 resident workgroups per XCD (one per CU): groups of 4
+// query tiles, so that the resident workgroups cover 4 x 8 tiles
+__device__ __forceinline__ void tile_of(int logical, int ntq, int ntk, int& tq, int& tk) {
+  constexpr int kGroup = 4;
+  const int span = kGroup * ntk;
+  const int g = logical / span;
+  const int first = g * kGroup;
+  const int rows = min(kGroup, ntq - first);
+  const int in_group = logical - g * span;
+  tq = first + in_group % rows;
+  tk = in_group / rows;
+}
+}  // namespace pp
+
+template <int HD, int MODE, int BLK>
+__global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int n_heads, int ldq, int ldk,
+    long long bsq, long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
+  constexpr int kCPH = HD / kChunk;
+  constexpr int kParts = (MODE == 1 && BLK == 128) ? kMaxHeadsHeadmax : 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[pp::kStages * pp::kStageBytes];
+  __shared__ float part[pp::kWaves][kParts];   // HEADMAX, 128-row blocks: per-head wave maxima
+  __shared__ float fin[pp::kWaves * 4];        // final per-(wave, sub-tile) values
+
+  const int T = gridDim.x;
+  const int logical = xcd_logical(blockIdx.y * T + blockIdx.x, T * gridDim.y);
+  const int seq = logical / T;
+  int tq, tk;
+  pp::tile_of(logical - seq * T, ntq, ntk, tq, tk);
+  Q += (size_t)seq * bsq;
+  K += (size_t)seq * bsk;
+  M += (size_t)seq * nb * nb;
+  const int q0 = tq * pp::kTQ, k0 = tk * pp::kTK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;   // waves w and w + 4 share a SIMD
+  const int wq = (wave >> 1) & 1, wk = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int qlo = q0 + grp * 128 + wq * 64, klo = k0 + wk * 64;
+  const bool mask_wave = klo == qlo;   // holds the i == j pairs of a diagonal block
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ring;
+  const int C = n_heads * kCPH;        // chunks; n_heads is even (launcher)
+
+  // ---- loads: instruction i of this wave fills LDS row 64 ii + drow of the
+  // Q (i < kDmaQ) or K region, physical piece lane % 8 (logical piece
+  // (lane % 8) ^ swz(row); the rows of one lane differ by 64, so one piece
+  // offset serves all of them)
+  const int drow = wave * 8 + (lane >> 3);
+  const uint32_t dpiece = (uint32_t)((((lane & 7) ^ swz(drow)) * 8) * 2);
+  uint32_t voff[pp::kDma];
+#pragma unroll
+  for (int i = 0; i < pp::kDma; ++i) {
+    const bool is_q = i < pp::kDmaQ;
+    const int ii = is_q ? i : i - pp::kDmaQ;
+    const int grow = min((is_q ? q0 : k0) + 64 * ii + drow, n_tokens - 1);   // rows past N: any valid row
+    voff[i] = (uint32_t)((size_t)grow * (is_q ? ldq : ldk) * 2) + dpiece;
+  }
+  // load i of chunk dc into the stage dc maps to; past the last chunk the
+  // last chunk's columns again
+  auto dma = [&](int dc, int i) {
+    const int cc = min(dc, C - 1);
+    const int col = (cc / kCPH) * HD + (cc % kCPH) * kChunk;
+    const bool is_q = i < pp::kDmaQ;
+    const int ii = is_q ? i : i - pp::kDmaQ;
+    const uint32_t base = lds0 + (uint32_t)((dc % pp::kStages) * pp::kStageBytes);
+    dma16(is_q ? (const void*)(Q + col) : (const void*)(K + col), voff[i],
+          base + (is_q ? 0u : (uint32_t)pp::kStageQ) + (uint32_t)((ii * pp::kWaves + wave) * 1024));
+  };
+
+  // ---- operand reads of one chunk: all four k-steps into registers
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int piece = (2 * s + hi) ^ swz(l32);
+    offA[s] = (uint32_t)((grp * 128 + wq * 64 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(pp::kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
+  }
+  lemo_bf16x8 fa[4][2], fb[4][2];   // [k-step][sub-tile row / column]
+  auto read_chunk = [&](int c) {
+    // the stage offset is opaque to the compiler, which would otherwise keep
+    // the read addresses of all three stages in registers
+    uint32_t so = (uint32_t)((c % pp::kStages) * pp::kStageBytes);
+    asm volatile("" : "+s"(so));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint8_t* pa = ring + offA[s] + so;
+      const uint8_t* pb = ring + offB[s] + so;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[s][i] = *reinterpret_cast<const lemo_bf16x8*>(pa + i * 32 * kRowBytes);
+        fb[s][i] = *reinterpret_cast<const lemo_bf16x8*>(pb + i * 32 * kRowBytes);
+      }
+    }
+  };
+
+  // PAPER: the two register sets of the running sum (see above); HEADMAX:
+  // acc holds the head's chain
+  lemo_f32x16 acc[2][2], sum[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sum[a][b][e] = 0.f;
+        acc[a][b][e] = 0.f;
+      }
+  float total[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // HEADMAX, blocks <= 64 rows: sum over heads
+
+  // Empty volatile asm pins a value to a point of the instruction stream.
+  // Volatile asm keeps its order with the barriers, so a phase's arithmetic
+  // (which the barriers alone would not hold in place: the compiler moved a
+  // fold into the neighbouring matrix phase) stays between its barriers.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
+  };
+  auto pin_sum = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(sum[a][b]));
+  };
+
+  // A matrix phase: the 16 MFMAs of the chunk in fa/fb (FIRST: the head's
+  // first chunk) for a head of parity P, with this wave's loads of chunk dc
+  // (none if dc < 0) issued one after every second MFMA, where they wait for
+  // the vector memory path under queued MFMAs.  The raised wave priority
+  // lets these MFMAs issue ahead of the other wave's reads and VALU work.
+  auto compute = [&](auto FIRST_, auto P_, int dc) {
+    constexpr bool FIRST = decltype(FIRST_)::value;
+    constexpr int P = decltype(P_)::value;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(fa[s][i]), "+v"(fb[s][i]));
+    pin_acc();
+    if (MODE == 0) pin_sum();
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          if (MODE == 0) {
+            lemo_f32x16& d = P == 0 ? acc[a][b] : sum[a][b];
+            lemo_f32x16& c0 = P == 0 ? sum[a][b] : acc[a][b];
+            if (FIRST && s == 0)   // the s_nop covers the wait after the fold's VALU writes of c0
+              asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3"
+                           : "=&v"(d)
+                           : "v"(fa[s][a]), "v"(fb[s][b]), "v"(c0));
+            else
+              d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][a], fb[s][b], d, 0, 0, 0);
+          } else {
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                fa[s][a], fb[s][b], (FIRST && s == 0) ? lemo_f32x16{} : acc[a][b], 0, 0, 0);
+          }
+          const int m = s * 4 + a * 2 + b;
+          if ((m & 1) && m / 2 < pp::kDma) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (dc >= 0) dma(dc, m / 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+    __builtin_amdgcn_s_setprio(0);
+    pin_acc();
+    if (MODE == 0) pin_sum();
+  };
+
+  auto exclude = [&](lemo_f32x16& v, int a, int b) {   // the i == j pairs of sub-tile (a, a)
+    if (a == b) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (acc_row(lane, e) == l32) v[e] = 0.f;
+    }
+  };
+  // folds head h, which ran with parity P
+  auto fold = [&](auto P_, int h) {
+    constexpr int P = decltype(P_)::value;
+    pin_acc();
+    if (MODE == 0) {
+      pin_sum();
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          lemo_f32x16& d = P == 0 ? acc[a][b] : sum[a][b];
+          const lemo_f32x16& o = P == 0 ? sum[a][b] : acc[a][b];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d[e] = __int_as_float(imax(__float_as_int(d[e]), __float_as_int(o[e])));
+        }
+      pin_sum();
+      pin_acc();
+    } else {
+      if (mask_wave) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) exclude(acc[a][b], a, b);
+      }
+      if (BLK >= 64) {
+        int m = 0;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+        m = wave_imax(m);
+        if (BLK == 128) {
+          if (lane == 0 && h >= 0) part[wave][h] = __int_as_float(m);
+        } else {
+          total[0][0] += __int_as_float(m);
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            int m = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+            total[a][b] += __int_as_float(wave_imax(m));
+          }
+      }
+    }
+  };
+
+  // ---- prologue: chunks 0-2 in flight, chunk 0 landed
+#pragma unroll
+  for (int c = 0; c < 3; ++c)
+#pragma unroll
+    for (int i = 0; i < pp::kDma; ++i) dma(c, i);
+  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+
+  // Each group runs its own copy of the loop (the same barriers, the same
+  // number of times), so no value is merged between the groups' paths.
+  auto run = [&](auto G_) {
+    constexpr int G = decltype(G_)::value;
+    auto chunk = [&](int h, auto KC_, auto P_) {
+      constexpr int kc = decltype(KC_)::value;
+      constexpr int P = decltype(P_)::value;
+      const int c = h * kCPH + kc;
+      // phase 2c: group 0 multiplies chunk c, with its loads of chunk c + 2
+      // (chunks 0-2 came with the prologue); group 1 reads chunk c, then
+      // folds its previous head while the reads are in flight (both sets
+      // start at zero, so the fold before the first head changes nothing)
+      if (G == 0) {
+        compute(std::integral_constant<bool, kc == 0>{}, P_, c >= 1 ? c + 2 : -1);
+      } else {
+        read_chunk(c);
+        if (kc == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          fold(std::integral_constant<int, 1 - P>{}, h - 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2c+1: group 1 multiplies chunk c, with its loads of chunk
+      // c + 3; group 0 reads chunk c+1 and folds head h after its last chunk
+      if (G == 1) {
+        compute(std::integral_constant<bool, kc == 0>{}, P_, c + 3);
+      } else {
+        if (c + 1 < C) read_chunk(c + 1);
+        if (kc == kCPH - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          fold(P_, h);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto head = [&](int h, auto P_) {
+      chunk(h, std::integral_constant<int, 0>{}, P_);
+      if (kCPH == 2) chunk(h, std::integral_constant<int, kCPH - 1>{}, P_);
+    };
+    if (G == 0) read_chunk(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < n_heads; h += 2) {
+      head(h, std::integral_constant<int, 0>{});
+      head(h + 1, std::integral_constant<int, 1>{});
+    }
+    if (G == 1) fold(std::integral_constant<int, 1>{}, n_heads - 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated loads past the last chunk
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+
+  // ---- per-(wave, sub-tile) block values -> fin[]; PAPER: an even head
+  // count leaves the sum in the odd heads' set, sum[]
+  if (MODE == 0) {
+    if (mask_wave) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) exclude(sum[a][b], a, b);
+    }
+    if (BLK >= 64) {
+      int m = 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(sum[a][b][e]));
+      m = wave_imax(m);
+      if (lane == 0) fin[wave * 4] = __int_as_float(m);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          int m = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(sum[a][b][e]));
+          m = wave_imax(m);
+          if (lane == 0) fin[wave * 4 + a * 2 + b] = __int_as_float(m);
+        }
+    }
+  } else if (BLK == 64) {
+    if (lane == 0) fin[wave * 4] = total[0][0];
+  } else if (BLK == 32) {
+    if (lane == 0) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) fin[wave * 4 + a * 2 + b] = total[a][b];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the parts of each block of this tile and write M
+  constexpr int kBQ = pp::kTQ / BLK, kBK = pp::kTK / BLK;
+  if (tid < kBQ * kBK) {
+    const int lq = tid / kBK, lk = tid % kBK;
+    const int bq = q0 / BLK + lq, bk = k0 / BLK + lk;
+    if (bq < nb && bk < nb) {
+      float val = 0.f;
+      if (MODE == 1 && BLK == 128) {
+        // the four waves of group lq cover this block; heads summed in order
+        for (int h = 0; h < n_heads; ++h) {
+          float m = 0.f;
+          for (int w = 4 * lq; w < 4 * lq + 4; ++w) m = fmaxf(m, part[w][h]);
+          val += m;
+        }
+      } else {
+        // sub-tile (a, b) of wave (g, wq, wk) covers query rows
+        // 128 g + 64 wq + 32 a and key rows 64 wk + 32 b of the tile
+        for (int p = 0; p < pp::kWaves * 4; ++p) {
+          const int w = p >> 2, a = (p >> 1) & 1, b = p & 1;
+          if (BLK >= 64 && (a | b)) continue;
+          const int rq = ((w >> 2) * 128 + ((w >> 1) & 1) * 64 + a * 32) / BLK;
+          const int rk = ((w & 1) * 64 + b * 32) / BLK;
+          if (rq == lq && rk == lk) val = fmaxf(val, fin[p]);
+        }
+      }
+      M[(size_t)bq * nb + bk] = val * out_scale;
+    }
+  }
+}
+
 // One head (the per-token predictor's q_hat, k_hat of width r): PAPER and
 // HEADMAX coincide, M = max(0, block max of S), and a tile has only
 // HD / 64 chunks, so a workgroup walks `per_wg` consecutive logical tiles
@@ -803,6 +1222,38 @@ hipError_t launch_one_head_mask(const uint16_t* q, const uint16_t* k, int n_batc
 }
 
 template <int HD, int MODE>
+hipError_t launch_pp(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk, long long bsq,
+                     long long bsk, int block, float scale, float* m, int nb, hipStream_t st) {
+  const int ntq = (n + pp::kTQ - 1) / pp::kTQ, ntk = (n + pp::kTK - 1) / pp::kTK;
+  const dim3 grid(ntq * ntk, n_batch), blk(pp::kThreads);
+  switch (block) {
+    case 32:
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 32>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale, m,
+                         nb, ntq, ntk);
+      break;
+    case 64:
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 64>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale, m,
+                         nb, ntq, ntk);
+      break;
+    default:
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 128>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale,
+                         m, nb, ntq, ntk);
+      break;
+  }
+  return hipGetLastError();
+}
+
+// The eight-wave kernel takes full launches (no causal mask, whole blocks)
+// with an even head count, at least 16 chunks per tile (below that its
+// per-tile start weighs more than it saves) and at least 512 of its tiles
+// (two per CU; smaller launches leave CUs idle with one workgroup per CU).
+bool use_pp(int n_batch, int n, int h, int hd) {
+  const long long tiles = (long long)((n + pp::kTQ - 1) / pp::kTQ) * ((n + pp::kTK - 1) / pp::kTK);
+  return h % 2 == 0 && (long long)h * (hd / kChunk) >= 16 && tiles * n_batch >= 512 &&
+         tiles * pp::kThreads <= 0x7fffffffLL;
+}
+
+template <int HD, int MODE>
 hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
                           long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
                           hipStream_t st) {
@@ -810,6 +1261,8 @@ hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int
     return launch_variant<HD, MODE, kMaskCausal>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
   if (n % block)
     return launch_variant<HD, MODE, kMaskRagged>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  if (use_pp(n_batch, n, h, HD))
+    return launch_pp<HD, MODE>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
   return launch_variant<HD, MODE, kMaskDiag>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
 }
 
