@@ -228,7 +228,7 @@ def main():
             "mlp_width": wm, "head_reduce": args.head_reduce, "select": "mean",
         },
         "roofline": {
-            "kernel": "lemo_block_scores (k_block_scores + column sum)",
+            "kernel": "lemo_block_scores (k_block_scores_pp + column sum)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
