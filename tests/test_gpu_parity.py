@@ -1283,6 +1283,10 @@ FUSED = [
     (1024, 256, 256, 64, 0.4, 256, 0),
     (640, 64, 200, 32, 1.0, 1, 0),        # keep all, ragged d_out
     (512, 128, 128, 64, 0.0, 64, 3),      # keep none
+    # output widths that are a multiple of 256 run the ping-pong form
+    (1024, 512, 512, 32, 0.3, 64, 5),
+    (768, 256, 256, 64, 0.0, 64, 3),      # keep none
+    (2048, 128, 768, 16, 0.7, 256, 0),    # three column tiles, two reduction chunks
 ]
 
 
@@ -1355,8 +1359,9 @@ def test_linear_scatter(case):
         assert torch.equal(r2, rd)
 
 
-def test_fused_bad_kept_and_capacity():
-    n, din, dout, b = 256, 64, 64, 16
+@pytest.mark.parametrize("din,dout", [(64, 64), (128, 256)], ids=["tile", "pingpong"])
+def test_fused_bad_kept_and_capacity(din, dout):
+    n, b = 256, 16
     rng = np.random.default_rng(41)
     x = synth.random_bf16(rng, (n, din))
     w = synth.random_bf16(rng, (dout, din), 0.125)
