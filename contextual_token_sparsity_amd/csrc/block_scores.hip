@@ -605,9 +605,39 @@ __device__ __forceinline__ void tile_of(int logical, int ntq, int ntk, int& tq, 
   tq = first + in_group % rows;
   tk = in_group / rows;
 }
+
+// Causal launches (N a multiple of 256, so 2 ntq key tiles): the tiles
+// (tq, tk) with tk <= 2 tq + 1, i.e. those holding a pair j < i, ntq (ntq + 1)
+// of them.  Groups of 4 query tiles as above; the tiles of the query tiles
+// before group g number 4g (4g + 1) (query tile t has 2t + 2), and inside a
+// group the key tiles up to 2 first + 1 are full columns of the group's rows,
+// then each pair of columns loses the group's top row.
+__device__ __forceinline__ void tri_tile_of(int logical, int ntq, int& tq, int& tk) {
+  int g = (int)((__builtin_sqrtf(1.f + 16.f * (float)logical) - 1.f) * 0.125f);   // 16 g^2 + 4 g <= logical
+  while (g > 0 && 4 * g * (4 * g + 1) > logical) --g;
+  while (4 * (g + 1) < ntq && 4 * (g + 1) * (4 * (g + 1) + 1) <= logical) ++g;
+  const int first = 4 * g;
+  const int rows = min(4, ntq - first);
+  int idx = logical - first * (first + 1);
+  const int full = rows * (2 * first + 2);
+  if (idx < full) {
+    tk = idx / rows;
+    tq = first + idx % rows;
+    return;
+  }
+  idx -= full;
+  int j = 0;   // columns 2 first + 2 + 2j and + 1 hold rows first + 1 + j .. first + rows - 1
+  while (idx >= 2 * (rows - 1 - j)) {
+    idx -= 2 * (rows - 1 - j);
+    ++j;
+  }
+  const int n = rows - 1 - j;
+  tk = 2 * first + 2 + 2 * j + idx / n;
+  tq = first + 1 + j + idx % n;
+}
 }  // namespace pp
 
-template <int HD, int MODE, int BLK>
+template <int HD, int MODE, int BLK, bool CAUSAL>
 __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int n_heads, int ldq, int ldk,
     long long bsq, long long bsk, float out_scale, float* __restrict__ M, int nb, int ntq, int ntk) {
@@ -621,7 +651,10 @@ __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
   const int logical = xcd_logical(blockIdx.y * T + blockIdx.x, T * gridDim.y);
   const int seq = logical / T;
   int tq, tk;
-  pp::tile_of(logical - seq * T, ntq, ntk, tq, tk);
+  if (CAUSAL)
+    pp::tri_tile_of(logical - seq * T, ntq, tq, tk);
+  else
+    pp::tile_of(logical - seq * T, ntq, ntk, tq, tk);
   Q += (size_t)seq * bsq;
   K += (size_t)seq * bsk;
   M += (size_t)seq * nb * nb;
@@ -632,7 +665,9 @@ __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
   const int wq = (wave >> 1) & 1, wk = wave & 1;
   const int l32 = lane & 31, hi = lane >> 5;
   const int qlo = q0 + grp * 128 + wq * 64, klo = k0 + wk * 64;
-  const bool mask_wave = klo == qlo;   // holds the i == j pairs of a diagonal block
+  // does this wave's 64 x 64 square hold a pair that takes no part: i == j
+  // (a diagonal block), or j >= i when causal
+  const bool mask_wave = CAUSAL ? klo >= qlo : klo == qlo;
   const uint32_t lds0 = (uint32_t)(uintptr_t)ring;
   const int C = n_heads * kCPH;        // chunks; n_heads is even (launcher)
 
@@ -765,11 +800,25 @@ __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
     if (MODE == 0) pin_sum();
   };
 
-  auto exclude = [&](lemo_f32x16& v, int a, int b) {   // the i == j pairs of sub-tile (a, a)
-    if (a == b) {
+  // zeroes the pairs of sub-tile (a, b) that take no part: i == j on the
+  // diagonal sub-tiles, or (causal) every j >= i.  Element e of this lane
+  // pairs query row qb + r_e with key row kr; the empty asm keeps the compares
+  // from being hoisted out of the head loop as live lane masks.
+  auto exclude = [&](lemo_f32x16& v, int a, int b) {
+    if (!CAUSAL) {
+      if (a == b) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(lane, e) == l32) v[e] = 0.f;
+      }
+    } else {
+      int qb = qlo + a * 32 + 4 * hi;
+      int kr = klo + b * 32 + l32;
+      asm volatile("" : "+v"(qb), "+v"(kr));
+      const int dq = kr - qb;   // j >= i at r_e <= dq
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (acc_row(lane, e) == l32) v[e] = 0.f;
+        if (8 * (e >> 2) + (e & 3) <= dq) v[e] = 0.f;
     }
   };
   // folds head h, which ran with parity P
@@ -958,6 +1007,8 @@ __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
         }
       }
       M[(size_t)bq * nb + bk] = val * out_scale;
+      // causal: the mirror block above the diagonal has no pair with j < i
+      if (CAUSAL && bq > bk) M[(size_t)bk * nb + bq] = 0.f;
     }
   }
 }
@@ -1221,48 +1272,53 @@ hipError_t launch_one_head_mask(const uint16_t* q, const uint16_t* k, int n_batc
   return launch_one_head<HD, kMaskDiag>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
 }
 
-template <int HD, int MODE>
+template <int HD, int MODE, bool CAUSAL>
 hipError_t launch_pp(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk, long long bsq,
                      long long bsk, int block, float scale, float* m, int nb, hipStream_t st) {
   const int ntq = (n + pp::kTQ - 1) / pp::kTQ, ntk = (n + pp::kTK - 1) / pp::kTK;
-  const dim3 grid(ntq * ntk, n_batch), blk(pp::kThreads);
+  const dim3 grid(CAUSAL ? ntq * (ntq + 1) : ntq * ntk, n_batch), blk(pp::kThreads);
   switch (block) {
     case 32:
-      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 32>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale, m,
-                         nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 32, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
     case 64:
-      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 64>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale, m,
-                         nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 64, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
     default:
-      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 128>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk, scale,
-                         m, nb, ntq, ntk);
+      hipLaunchKernelGGL((k_block_scores_pp<HD, MODE, 128, CAUSAL>), grid, blk, 0, st, q, k, n, h, ldq, ldk, bsq, bsk,
+                         scale, m, nb, ntq, ntk);
       break;
   }
   return hipGetLastError();
 }
 
-// The eight-wave kernel takes full launches (no causal mask, whole blocks)
-// with an even head count, at least 16 chunks per tile (below that its
-// per-tile start weighs more than it saves) and at least 512 of its tiles
-// (two per CU; smaller launches leave CUs idle with one workgroup per CU).
-bool use_pp(int n_batch, int n, int h, int hd) {
-  const long long tiles = (long long)((n + pp::kTQ - 1) / pp::kTQ) * ((n + pp::kTK - 1) / pp::kTK);
+// The eight-wave kernel takes launches without a ragged last block, with an
+// even head count, at least 16 chunks per tile (below that its per-tile
+// start weighs more than it saves) and at least 512 of its tiles (two per
+// CU; smaller launches leave CUs idle with one workgroup per CU); causal
+// launches also need N to be a multiple of its 256-row tile.
+bool use_pp(int n_batch, int n, int h, int hd, bool causal) {
+  const long long ntq = (n + pp::kTQ - 1) / pp::kTQ, ntk = (n + pp::kTK - 1) / pp::kTK;
+  const long long tiles = causal ? ntq * (ntq + 1) : ntq * ntk;
   return h % 2 == 0 && (long long)h * (hd / kChunk) >= 16 && tiles * n_batch >= 512 &&
-         tiles * pp::kThreads <= 0x7fffffffLL;
+         tiles * pp::kThreads <= 0x7fffffffLL && (!causal || n % pp::kTQ == 0);
 }
 
 template <int HD, int MODE>
 hipError_t launch_hd_mode(const uint16_t* q, const uint16_t* k, int n_batch, int n, int h, int ldq, int ldk,
                           long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
                           hipStream_t st) {
-  if (causal)
+  if (causal) {
+    if (use_pp(n_batch, n, h, HD, true))
+      return launch_pp<HD, MODE, true>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
     return launch_variant<HD, MODE, kMaskCausal>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  }
   if (n % block)
     return launch_variant<HD, MODE, kMaskRagged>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
-  if (use_pp(n_batch, n, h, HD))
-    return launch_pp<HD, MODE>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
+  if (use_pp(n_batch, n, h, HD, false))
+    return launch_pp<HD, MODE, false>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
   return launch_variant<HD, MODE, kMaskDiag>(q, k, n_batch, n, h, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
 }
 

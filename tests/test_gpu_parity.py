@@ -245,6 +245,50 @@ def test_exact_eight_wave_sampled(shape, mode):
         _sampled_check(q[s], k[s], h, hd, b, mode, entries, [int(rng.integers(0, nb)), nb - 1], Mg[s], Ig[s])
 
 
+EIGHT_WAVE_CAUSAL = [
+    # (B, N, H, hd, block): causal launches the eight-wave kernel takes (N a
+    # multiple of 256, >= 512 of its tiles on or below the diagonal)
+    (2, 4096, 8, 128, 64),     # 2 x 272 tiles
+    (1, 6144, 16, 64, 32),     # 600 tiles, 32-row blocks, head_dim 64
+    (1, 6144, 8, 128, 128),    # 128-row blocks span a group's four waves
+    (1, 6144, 128, 64, 128),   # HEADMAX's most heads: per-head maxima in LDS
+]
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+@pytest.mark.parametrize("shape", EIGHT_WAVE_CAUSAL, ids=lambda s: "B%d_N%d_H%d_hd%d_b%d" % s)
+def test_exact_eight_wave_causal_sampled(shape, mode):
+    """The eight-wave kernel's causal launches against the oracle's causal
+    scores: every entry written (M pre-filled with -1), every block above the
+    diagonal 0, sampled blocks on, next to and below the diagonal, and two
+    whole columns with their column scores."""
+    B, n, h, hd, b = shape
+    say("eight-wave causal", shape, mode)
+    q, k = rand_batch(6500 + n + h + b, B, n, h, hd)
+    nb = n // b
+    M = torch.full((B, nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), h, hd, b, mode, causal=True, block_scores=M)
+    torch.cuda.synchronize()
+    Mg, Ig = M.cpu().numpy(), I.cpu().numpy()
+    assert (Mg >= 0).all()
+    upper = np.triu_indices(nb, 1)
+    rng = np.random.default_rng(n + b + 1)
+    entries = [(0, 0), (1, 1), (1, 0), (nb - 1, nb - 1), (nb - 1, nb - 2), (nb - 1, 0), (nb // 2, nb // 2)]
+    entries += [tuple(sorted(int(x) for x in rng.integers(0, nb, 2))[::-1]) for _ in range(8)]
+    for s in range(B):
+        assert not Mg[s][upper].any()
+        for (r, c) in entries:
+            M_ref, _ = O.exact_block_scores(q[s], k[s], h, hd, b, mode, query_blocks=[r], key_blocks=[c], causal=True)
+            ok, worst = scores_close([Mg[s, r, c]], M_ref[0])
+            assert ok and worst < 1e-4, (s, r, c, Mg[s, r, c], M_ref[0, 0])
+        for c in (int(rng.integers(0, nb)), 0):
+            I_ref, col = O.exact_column_score(q[s], k[s], h, hd, b, mode, c, causal=True)
+            ok, worst = scores_close(Mg[s][:, c], col)
+            assert ok, (s, c, worst)
+            ok, worst = scores_close([Ig[s, c]], [I_ref])
+            assert ok and worst < 1e-4, (s, c, Ig[s, c], I_ref)
+
+
 def test_exact_eight_wave_deterministic():
     """Two launches of the eight-wave kernel give the same bits."""
     q, k = rand_qk(78, 4096, 8, 128)
@@ -394,12 +438,10 @@ def test_causal_closed_form_full_size(mode, n):
 
 def test_causal_full_size_sampled():
     """The 7B N=16K exact workload, causal, in the benchmark's launch
-    configuration: sampled block scores and whole columns from the oracle.
-    Below the block diagonal the causal kernel computes the same pairs as the
-    full-attention call (the eight-wave kernel at this shape): HEADMAX runs
-    the same MFMA chains in both, so those entries agree bit for bit; PAPER's
-    eight-wave form accumulates each head onto the running sum (the same sum
-    in another fp32 order), so they agree to fp32 accumulation error."""
+    configuration: sampled block scores and whole columns from the oracle;
+    below the block diagonal the causal launch runs the same MFMA chains as
+    the full one (the eight-wave kernel in both), so those entries equal the
+    full-attention call bit for bit."""
     w = synth.WORKLOADS["llama2-7b-n16k"]
     say("causal full size")
     L = synth.make_layer(w.n_tokens, w.d_model, w.block, w.seed, n_heads=w.n_heads, head_dim=w.head_dim,
@@ -428,11 +470,7 @@ def test_causal_full_size_sampled():
             assert ok and worst < 1e-4, (c, Ig[c], I_ref)
         Mf = torch.empty((nb, nb), device="cuda")
         lemo.lemo_block_scores(qd, kd, w.n_heads, w.head_dim, w.block, mode, block_scores=Mf)
-        if mode == O.REDUCE_HEADMAX:
-            assert np.array_equal(Mg[lower], Mf.cpu().numpy()[lower])
-        else:
-            a, f = Mg[lower].astype(np.float64), Mf.cpu().numpy()[lower].astype(np.float64)
-            assert np.all(np.abs(a - f) <= 1e-5 * np.abs(f)), float(np.max(np.abs(a - f) / np.abs(f)))
+        assert np.array_equal(Mg[lower], Mf.cpu().numpy()[lower])
         assert not Mg[np.triu_indices(nb, 1)].any()
 
 
