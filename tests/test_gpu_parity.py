@@ -289,6 +289,50 @@ def test_exact_eight_wave_causal_sampled(shape, mode):
             assert ok and worst < 1e-4, (s, c, Ig[s, c], I_ref)
 
 
+DISPATCH_EDGES = [
+    # (B, N, H, hd, block, causal): on either side of the eight-wave kernel's
+    # launch conditions (even head count, >= 16 chunks per tile, >= 512 of
+    # its tiles, causal N a multiple of 256); each side against the oracle
+    (1, 4096, 9, 128, 64, False),    # odd head count: four-wave kernel
+    (1, 4096, 14, 64, 64, False),    # 14 chunks per tile: four-wave kernel
+    (1, 3840, 8, 128, 64, False),    # 450 tiles: four-wave kernel
+    (1, 4096, 8, 128, 64, False),    # 512 tiles: eight-wave kernel
+    (1, 5632, 8, 128, 64, True),     # 506 causal tiles: four-wave kernel
+    (1, 5888, 8, 128, 64, True),     # 552 causal tiles: eight-wave kernel
+    (1, 6016, 8, 128, 64, True),     # N not a multiple of 256: four-wave kernel
+]
+
+
+@pytest.mark.parametrize("mode", [O.REDUCE_PAPER, O.REDUCE_HEADMAX], ids=["paper", "headmax"])
+@pytest.mark.parametrize("shape", DISPATCH_EDGES,
+                         ids=lambda s: "B%d_N%d_H%d_hd%d_b%d_%s" % (*s[:5], "causal" if s[5] else "full"))
+def test_exact_dispatch_edges_sampled(shape, mode):
+    B, n, h, hd, b, causal = shape
+    say("dispatch edge", shape, mode)
+    q, k = rand_batch(6900 + n + h, B, n, h, hd)
+    nb = n // b
+    M = torch.full((B, nb, nb), -1.0, device="cuda")
+    I, _ = lemo.lemo_block_scores_batched(dev(q), dev(k), h, hd, b, mode, causal=causal, block_scores=M)
+    torch.cuda.synchronize()
+    Mg, Ig = M.cpu().numpy()[0], I.cpu().numpy()[0]
+    assert (Mg >= 0).all()
+    if causal:
+        assert not Mg[np.triu_indices(nb, 1)].any()
+    rng = np.random.default_rng(n + h)
+    entries = [(0, 0), (nb - 1, nb - 1), (nb - 1, 0), (nb // 2, nb // 2 - 1)]
+    entries += [tuple(sorted(int(x) for x in rng.integers(0, nb, 2))[::-1]) for _ in range(4)]
+    for (r, c) in entries:
+        M_ref, _ = O.exact_block_scores(q[0], k[0], h, hd, b, mode, query_blocks=[r], key_blocks=[c], causal=causal)
+        ok, worst = scores_close([Mg[r, c]], M_ref[0])
+        assert ok and worst < 1e-4, (r, c, Mg[r, c], M_ref[0, 0])
+    c = int(rng.integers(0, nb))
+    I_ref, col = O.exact_column_score(q[0], k[0], h, hd, b, mode, c, causal=causal)
+    ok, worst = scores_close(Mg[:, c], col)
+    assert ok, (c, worst)
+    ok, worst = scores_close([Ig[c]], [I_ref])
+    assert ok and worst < 1e-4, (c, Ig[c], I_ref)
+
+
 def test_exact_eight_wave_deterministic():
     """Two launches of the eight-wave kernel give the same bits."""
     q, k = rand_qk(78, 4096, 8, 128)
