@@ -333,6 +333,32 @@ def test_exact_dispatch_edges_sampled(shape, mode):
     assert ok and worst < 1e-4, (c, Ig[c], I_ref)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_exact_eight_wave_strided(causal):
+    """The eight-wave kernel on Q and K read from wider rows (ld > H*hd, e.g.
+    slices of a fused QKV) with NaN in every column it must not read:
+    bit-equal to the same call on dense copies, and sampled blocks against the
+    oracle."""
+    n, h, hd, b = 6144, 8, 128, 64
+    say("eight-wave strided", causal)
+    q, k = rand_qk(6950, n, h, hd)
+    nb = n // b
+    Md = torch.empty((1, nb, nb), device="cuda")
+    lemo.lemo_block_scores_batched(dev(q), dev(k), h, hd, b, O.REDUCE_PAPER, causal=causal, block_scores=Md)
+    qp, kp = padded(q, 1160, 0x7FC0), padded(k, 1096, 0x7FC0)   # NaN in the unused columns
+    Ms = torch.empty((1, nb, nb), device="cuda")
+    lemo.lemo_block_scores_batched(qp[:, :h * hd], kp[:, :h * hd], h, hd, b, O.REDUCE_PAPER, causal=causal,
+                                   block_scores=Ms)
+    torch.cuda.synchronize()
+    assert torch.equal(Md, Ms)
+    Mg = Ms.cpu().numpy()[0]
+    for (r, c) in ((0, 0), (nb - 1, nb - 1), (nb - 1, 3), (40, 17)):
+        M_ref, _ = O.exact_block_scores(q, k, h, hd, b, O.REDUCE_PAPER, query_blocks=[r], key_blocks=[c],
+                                        causal=causal)
+        ok, worst = scores_close([Mg[r, c]], M_ref[0])
+        assert ok and worst < 1e-4, (r, c, Mg[r, c], M_ref[0, 0])
+
+
 def test_exact_eight_wave_deterministic():
     """Two launches of the eight-wave kernel give the same bits."""
     q, k = rand_qk(78, 4096, 8, 128)
