@@ -1013,7 +1013,9 @@ __global__ __launch_bounds__(pp::kThreads, 1) void k_block_scores_pp(
   }
 }
 
-// One head (the per-token predictor's q_hat, k_hat of width r): PAPER and
+// One head (the per-token predictor's q_hat, k_hat of width r; full launches
+// of one sequence with blocks of 32 or 64 and N a multiple of 1024 run
+// k_scores_one_head_pp below): PAPER and
 // HEADMAX coincide, M = max(0, block max of S), and a tile has only
 // HD / 64 chunks, so a workgroup walks `per_wg` consecutive logical tiles
 // with the loads of the next tile's first chunk in flight during the current
@@ -1186,6 +1188,243 @@ __global__ __launch_bounds__(kThreads, 2) void k_scores_one_head(
   }
 }
 
+// Eight-wave form of the one-head scores (full launches, blocks of 32 or
+// 64 rows, N a multiple of 1024): one workgroup per CU walks tiles rank,
+// rank + G, rank + 2G, ... of the 256 x 128 tile order of k_block_scores_pp
+// (G workgroups, XCD ranges as in a plain launch of G), with the same two
+// wave groups, phases, ring and loads; the load stream runs on across tile
+// boundaries.  A tile is kCPH chunks; when a group has multiplied a tile's
+// last chunk, its next memory phase reduces the tile to block maxima (the
+// exclusions first, on diagonal squares) and writes them: with blocks of 64
+// rows or fewer each wave holds whole blocks.  Each wave keeps two cursors
+// over its tiles, one for the loads and one for the output, stepped without
+// division: in the tile order (groups of 4 query tiles, 4 ntk tiles each),
+// adding G to a tile's index moves it G positions within its group, with a
+// carry into the next group.
+template <int HD, int BLK>
+__global__ __launch_bounds__(pp::kThreads, 1) void k_scores_one_head_pp(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int n_tokens, int ldq, int ldk, float out_scale,
+    float* __restrict__ M, int nb, int ntk, int total) {
+  constexpr int kCPH = HD / kChunk;
+  static_assert(BLK == 32 || BLK == 64, "blocks within one wave's square");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[pp::kStages * pp::kStageBytes];
+  const int G = gridDim.x;
+  const int rank = xcd_logical(blockIdx.x, G);
+  const int U = (total - rank + G - 1) / G;   // this workgroup's tiles (>= 1: G <= total)
+  const int C = U * kCPH;                     // its chunks
+  const int span = 4 * ntk;                   // tiles per group of 4 query tiles
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wq = (wave >> 1) & 1, wk = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)ring;
+
+  // a cursor over this workgroup's tiles: group index and position in group
+  struct Cursor {
+    int unit, g, pos;
+  };
+  auto cursor_at0 = [&]() { return Cursor{0, rank / span, rank % span}; };
+  auto advance = [&](Cursor& cu) {
+    if (cu.unit + 1 >= U) return;   // stays on the last tile (the repeated loads)
+    ++cu.unit;
+    cu.pos += G;
+    while (cu.pos >= span) {
+      cu.pos -= span;
+      ++cu.g;
+    }
+  };
+  auto q0_of = [&](const Cursor& cu) { return (4 * cu.g + (cu.pos & 3)) * pp::kTQ; };
+  auto k0_of = [&](const Cursor& cu) { return (cu.pos >> 2) * pp::kTK; };
+
+  const int drow = wave * 8 + (lane >> 3);
+  const uint32_t dpiece = (uint32_t)((((lane & 7) ^ swz(drow)) * 8) * 2);
+  Cursor dcur = cursor_at0();   // the tile of the next chunk this wave loads
+  int dkc = 0;                  // and its chunk within the tile
+  // this wave's 6 loads of its next chunk (in order), into the stage chunk dc maps to
+  int dnext = 0;                // the chunk number of the next load batch
+  auto dma_one = [&](int i) {
+    const bool is_q = i < pp::kDmaQ;
+    const int ii = is_q ? i : i - pp::kDmaQ;
+    const int row = (is_q ? q0_of(dcur) : k0_of(dcur)) + 64 * ii + drow;
+    const uint32_t voff = (uint32_t)((size_t)row * (is_q ? ldq : ldk) * 2) + dpiece;
+    const uint32_t base = lds0 + (uint32_t)((dnext % pp::kStages) * pp::kStageBytes);
+    dma16(is_q ? (const void*)(Q + dkc * kChunk) : (const void*)(K + dkc * kChunk), voff,
+          base + (is_q ? 0u : (uint32_t)pp::kStageQ) + (uint32_t)((ii * pp::kWaves + wave) * 1024));
+  };
+  auto dma_done = [&]() {   // after the 6 loads of a chunk: step the load cursor
+    ++dnext;
+    if (dnext < C) {
+      if (++dkc == kCPH) {
+        dkc = 0;
+        advance(dcur);
+      }
+    }
+  };
+
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int piece = (2 * s + hi) ^ swz(l32);
+    offA[s] = (uint32_t)((grp * 128 + wq * 64 + l32) * kRowBytes + piece * 16);
+    offB[s] = (uint32_t)(pp::kStageQ + (wk * 64 + l32) * kRowBytes + piece * 16);
+  }
+  lemo_bf16x8 fa[4][2], fb[4][2];
+  auto read_chunk = [&](int c) {
+    uint32_t so = (uint32_t)((c % pp::kStages) * pp::kStageBytes);
+    asm volatile("" : "+s"(so));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint8_t* pa = ring + offA[s] + so;
+      const uint8_t* pb = ring + offB[s] + so;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[s][i] = *reinterpret_cast<const lemo_bf16x8*>(pa + i * 32 * kRowBytes);
+        fb[s][i] = *reinterpret_cast<const lemo_bf16x8*>(pb + i * 32 * kRowBytes);
+      }
+    }
+  };
+
+  lemo_f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) asm volatile("" : "+v"(acc[a][b]));
+  };
+  // a matrix phase over the chunk in fa/fb, with this wave's loads of its next
+  // chunk between the MFMAs when `loads`
+  auto compute = [&](auto FIRST_, bool loads) {
+    constexpr bool FIRST = decltype(FIRST_)::value;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(fa[s][i]), "+v"(fb[s][i]));
+    if (!FIRST) pin_acc();
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              fa[s][a], fb[s][b], (FIRST && s == 0) ? lemo_f32x16{} : acc[a][b], 0, 0, 0);
+          const int m = s * 4 + a * 2 + b;
+          if ((m & 1) && m / 2 < pp::kDma) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (loads) dma_one(m / 2);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+    __builtin_amdgcn_s_setprio(0);
+    pin_acc();
+    if (loads) dma_done();
+  };
+
+  // the block maxima of the tile at the output cursor, then the cursor steps
+  Cursor ocur = cursor_at0();
+  auto output = [&]() {
+    pin_acc();
+    const int qlo = q0_of(ocur) + grp * 128 + wq * 64, klo = k0_of(ocur) + wk * 64;
+    if (klo == qlo) {   // the i == j pairs of the diagonal sub-tiles
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (acc_row(lane, e) == l32) acc[a][a][e] = 0.f;
+    }
+    if (BLK == 32) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          int m = 0;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+          m = wave_imax(m);
+          if (lane == 0) M[(size_t)((qlo + 32 * a) / 32) * nb + (klo + 32 * b) / 32] = __int_as_float(m) * out_scale;
+        }
+    } else {
+      int m = 0;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = imax(m, __float_as_int(acc[a][b][e]));
+      m = wave_imax(m);
+      if (lane == 0) M[(size_t)(qlo / 64) * nb + klo / 64] = __int_as_float(m) * out_scale;
+    }
+    advance(ocur);
+  };
+
+  // prologue: chunks 0-2 in flight (C >= 3 is not required: past the last
+  // chunk the loads repeat it), chunk 0 landed
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+#pragma unroll
+    for (int i = 0; i < pp::kDma; ++i) dma_one(i);
+    dma_done();
+  }
+  asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+
+  auto run = [&](auto G_) {
+    constexpr int G2 = decltype(G_)::value;
+    auto chunk = [&](int c, auto KC_) {
+      constexpr int kc = decltype(KC_)::value;
+      // phase 2c: group 0 multiplies chunk c (with its loads of chunk c + 2
+      // from c = 1 on); group 1 reads chunk c, then outputs its last tile
+      if (G2 == 0) {
+        compute(std::integral_constant<bool, kc == 0>{}, c >= 1);
+      } else {
+        read_chunk(c);
+        if (kc == 0 && c > 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          output();
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2c+1: group 1 multiplies chunk c (with its loads of chunk
+      // c + 3); group 0 reads chunk c+1, then outputs the tile chunk c ends
+      if (G2 == 1) {
+        compute(std::integral_constant<bool, kc == 0>{}, true);
+      } else {
+        if (c + 1 < C) read_chunk(c + 1);
+        if (kc == kCPH - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          output();
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (G2 == 0) read_chunk(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = 0; c < C; c += kCPH) {
+      chunk(c, std::integral_constant<int, 0>{});
+      if (kCPH == 2) chunk(c + 1, std::integral_constant<int, kCPH - 1>{});
+    }
+    if (G2 == 1) output();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (grp == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+}
+
 // Column sums I[c] = sum_r M[r][c].  A workgroup owns 16 columns; its 256
 // threads split the rows into 16 interleaved slices (thread (slice, column)
 // adds rows slice, slice+16, ... in order), then one thread per column adds
@@ -1267,6 +1506,20 @@ template <int HD>
 hipError_t launch_one_head_mask(const uint16_t* q, const uint16_t* k, int n_batch, int n, int ldq, int ldk,
                                 long long bsq, long long bsk, int block, bool causal, float scale, float* m, int nb,
                                 hipStream_t st) {
+  // the eight-wave form: one sequence, no mask, blocks of 32 or 64 rows, N a
+  // multiple of 1024 (groups of 4 whole query tiles), at least 512 tiles
+  const long long tiles = (long long)(n / pp::kTQ) * (n / pp::kTK);
+  if (!causal && n_batch == 1 && n % 1024 == 0 && (block == 32 || block == 64) && tiles >= 512 &&
+      tiles <= 0x7fffffffLL) {
+    const int ntk = n / pp::kTK, grid = 256;
+    if (block == 32)
+      hipLaunchKernelGGL((k_scores_one_head_pp<HD, 32>), dim3(grid), dim3(pp::kThreads), 0, st, q, k, n, ldq, ldk,
+                         scale, m, nb, ntk, (int)tiles);
+    else
+      hipLaunchKernelGGL((k_scores_one_head_pp<HD, 64>), dim3(grid), dim3(pp::kThreads), 0, st, q, k, n, ldq, ldk,
+                         scale, m, nb, ntk, (int)tiles);
+    return hipGetLastError();
+  }
   if (causal) return launch_one_head<HD, kMaskCausal>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
   if (n % block) return launch_one_head<HD, kMaskRagged>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);
   return launch_one_head<HD, kMaskDiag>(q, k, n_batch, n, ldq, ldk, bsq, bsk, block, scale, m, nb, st);

@@ -417,9 +417,15 @@ ONE_HEAD_WALK = [
     # so each workgroup walks a range of several tiles (the next tile's first
     # chunk loading under the current tile's last)
     (1, 6144, 64, 128, False),     # 128-row blocks: the four waves' maxima meet in LDS per tile
-    (1, 6144, 128, 32, False),     # 32-row blocks: each wave writes its own four blocks
+    (1, 6016, 128, 32, False),     # 32-row blocks: each wave writes its own four blocks
     (2, 6000, 128, 64, False),     # batch of two ragged sequences
     (1, 8190, 64, 64, True),       # causal, ragged: 2080 tiles on or below the diagonal
+    # the eight-wave form (one sequence, no mask, blocks of 32 or 64, N a
+    # multiple of 1024, >= 512 tiles of 256 x 128): each workgroup walks
+    # tiles 256 apart, loads running on across tile boundaries
+    (1, 4096, 128, 64, False),     # 512 tiles: two per workgroup
+    (1, 4096, 64, 32, False),      # head_dim 64 (a tile is one chunk), 32-row blocks
+    (1, 8192, 128, 32, False),     # 2048 tiles, 32-row blocks
 ]
 
 
