@@ -48,8 +48,9 @@
 // value; every step is positively homogeneous so this is exact up to
 // rounding.
 //
-// Full launches (no causal mask, whole blocks) with an even head count and
-// enough tiles to fill the chip run k_block_scores_pp instead: one
+// Launches without a ragged last block, with an even head count and enough
+// tiles to fill the chip (causal ones with N a multiple of 256) run
+// k_block_scores_pp instead: one
 // eight-wave workgroup per CU on a 256 x 128 tile, whose two groups of four
 // waves take turns between matrix phases and memory phases (its comment
 // below gives the schedule).
@@ -550,9 +551,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_block_scores(
 }
 
 // ---------------------------------------------------------------------------
-// Eight-wave form of the same reduction (the launcher's choice for full,
-// unmasked launches with an even head count and enough tiles to fill the
-// chip).  One workgroup per CU owns a 256 x 128 tile (query rows x key
+// Eight-wave form of the same reduction (the launcher's choice for launches
+// without a ragged last block, with an even head count and enough tiles to
+// fill the chip; causal ones also need N to be a multiple of 256, and then
+// cover the tiles on or below the diagonal, with the exclusions and mirror
+// zeros of k_block_scores).  One workgroup per CU owns a 256 x 128 tile (query rows x key
 // rows): 25 % fewer refill bytes per MFMA than two 128 x 128 workgroups.
 // Its waves form two groups of four, one wave of each group per SIMD, each
 // group a 2 x 2 grid of 64 x 64 wave tiles (group g: query rows 128 g ..
