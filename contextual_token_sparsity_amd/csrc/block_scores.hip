@@ -1191,8 +1191,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_scores_one_head(
   }
 }
 
-// Eight-wave form of the one-head scores (full launches, blocks of 32 or
-// 64 rows, N a multiple of 1024): one workgroup per CU walks tiles rank,
+// Eight-wave form of the one-head scores (full launches of one sequence,
+// blocks of 32 or 64 rows, N a multiple of 1024, at least 512 tiles): one
+// workgroup per CU walks tiles rank,
 // rank + G, rank + 2G, ... of the 256 x 128 tile order of k_block_scores_pp
 // (G workgroups, XCD ranges as in a plain launch of G), with the same two
 // wave groups, phases, ring and loads; the load stream runs on across tile
