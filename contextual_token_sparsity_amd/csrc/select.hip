@@ -4,8 +4,10 @@
 //
 // One workgroup of 1024 threads (16 waves) handles up to 8192 blocks:
 //   * scores are staged in LDS;
-//   * the threshold is the caller's, the mean (float64 sum in block order by
-//     one lane, then divided and rounded to fp32), or implied by top-k;
+//   * the threshold is the caller's, the mean (float64 sum in block order,
+//     then divided and rounded to fp32), or implied by top-k.  The mean's sum
+//     is formed by a parallel reduction when every addition is exact (then
+//     every order gives the same sum), else by one lane in block order;
 //   * top-k: every score becomes an order-preserving 32-bit key (larger key
 //     = better score; -0 and +0 share a key as they compare equal; NaN gets
 //     the lowest key, below -inf), and the k-th largest key T is found by a
@@ -15,7 +17,8 @@
 //     whose key is T, the ones with the lowest indices (ties go to the lower
 //     block index), as many as k still needs; the reported threshold is the
 //     score of the last of them, the k-th best.  (This replaced ranking
-//     every block by counting the blocks that beat it, O(nb^2).)
+//     every block by counting the blocks that beat it, O(nb^2); counting
+//     ranks directly is slower even at 256 blocks.)
 //   * the ascending kept list is built 1024 blocks at a time: a wave ballot
 //     of the keep bits, the lane's prefix from the bits below it (mbcnt), and
 //     the waves' counts scanned through LDS; ties at T are counted the same
@@ -28,6 +31,15 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBlocks = 8192;
 constexpr int kPerThread = kMaxBlocks / kThreads;
+
+// Position of the lowest set bit of a finite nonzero double: v is an odd
+// multiple of 2^lowest_bit(v).
+__device__ __forceinline__ int lowest_bit(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int e = (int)((b >> 52) & 0x7ffu);
+  const unsigned long long m = (b & 0xfffffffffffffull) | (e ? (1ull << 52) : 0ull);
+  return (e ? e - 1075 : -1074) + __builtin_ctzll(m);
+}
 
 // Order-preserving key of a score: a > b as floats iff key(a) > key(b);
 // equal floats (including -0 and +0) share a key; every NaN gets 0, below
@@ -57,6 +69,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
   __shared__ int wave_cnt[kWaves];
   __shared__ int tie_cnt[kWaves];
   __shared__ uint32_t hist[256];
+  __shared__ double wsum[kWaves], wmag[kWaves];
+  __shared__ int wlsb[kWaves], wfin[kWaves];
   __shared__ int scan_tot[4];
   __shared__ uint32_t sel_key;
   __shared__ int sel_rem;
@@ -82,10 +96,60 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
   uint32_t T = 0;       // top-k: the k-th largest key
   int ties_kept = 0;    // top-k: how many blocks with key T are kept
   if (mode == 2) {
+    // Each score is a multiple of 2^lowest_bit.  When the magnitudes sum to
+    // less than 2^(b + 52), b the smallest such bit over the scores, every
+    // partial sum of any subset is a multiple of 2^b of magnitude below
+    // 2^(b + 53), so it is a float64 value: every addition is exact, in any
+    // order, and the tree sum below equals the sum in block order.  With a
+    // non-finite score, or a wider range, one lane sums in block order.
+    // Partial sums start at +0, as the sequential one does, so zeros of
+    // either sign give the same +0.
+    double part = 0.0, mag = 0.0;
+    int lsb = 0x7fffffff;
+    bool fin = true;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < nb) {
+        const double v = (double)s[c];
+        fin = fin && __builtin_isfinite(v);
+        if (v != 0.0 && __builtin_isfinite(v)) lsb = min(lsb, lowest_bit(v));
+        part += v;
+        mag += fabs(v);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      part += __shfl_xor(part, off, 64);
+      mag += __shfl_xor(mag, off, 64);
+      lsb = min(lsb, __shfl_xor(lsb, off, 64));
+    }
+    const bool wave_fin = __ballot(!fin) == 0ull;
+    if (lane == 0) {
+      wsum[wave] = part;
+      wmag[wave] = mag;
+      wlsb[wave] = lsb;
+      wfin[wave] = wave_fin ? 1 : 0;
+    }
+    __syncthreads();
     if (tid == 0) {
-      double acc = 0.0;
-      for (int c = 0; c < nb; ++c) acc += (double)s[c];
-      theta_sh = (float)(acc / (double)nb);
+      double total = 0.0, bound = 0.0;
+      int b = 0x7fffffff;
+      bool all_fin = true;
+      for (int w = 0; w < kWaves; ++w) {
+        total += wsum[w];
+        bound += wmag[w];
+        b = min(b, wlsb[w]);
+        all_fin = all_fin && wfin[w];
+      }
+      // 2^(b + 52) as a float64 (b >= -149 for float32 inputs, so it is normal)
+      const bool exact =
+          all_fin && (bound == 0.0 || bound < __longlong_as_double((long long)(b + 52 + 1023) << 52));
+      if (!exact) {
+        total = 0.0;
+        for (int c = 0; c < nb; ++c) total += (double)s[c];
+      }
+      theta_sh = (float)(total / (double)nb);
     }
   } else if (topk) {
 #pragma unroll

@@ -770,6 +770,36 @@ def test_select_edge_values():
     _select_case(same, O.SELECT_MEAN)
 
 
+def test_select_mean_sum_paths():
+    """The mean's float64 sum: exact inputs (every partial sum representable,
+    summed as a tree) and inputs whose sum in block order rounds (summed by one
+    lane in that order) both give the oracle's threshold bit for bit."""
+    rng = np.random.default_rng(11)
+    for nb in (3, 256, 1025, 8192):
+        # multiples of 2^-8 below 64, either sign: a span of at most 27 bits
+        s = (rng.integers(-2 ** 14, 2 ** 14, nb) / 256.0).astype(np.float32)
+        _select_case(s, O.SELECT_MEAN)
+        # a 2^60 term beside small ones: the sum in block order rounds
+        w = (rng.random(nb) * 4).astype(np.float32)
+        w[nb // 3] = np.float32(2.0 ** 60)
+        w[(2 * nb) // 3] = np.float32(-(2.0 ** 60))
+        _select_case(w, O.SELECT_MEAN)
+    # rounding decides the threshold: 2^60 + 1 - 2^60 is 0 in block order, 1 exactly
+    _select_case(np.array([2.0 ** 60, 1.0, -(2.0 ** 60)], np.float32), O.SELECT_MEAN)
+    # float32 subnormals beside normal scores, and zeros of both signs only
+    _select_case(np.array([1e-45, 3e-39, 0.5, 2.0], np.float32), O.SELECT_MEAN)
+    _select_case(np.array([-0.0, 0.0, -0.0], np.float32), O.SELECT_MEAN)
+
+
+@pytest.mark.parametrize("nb", [511, 512, 513])
+def test_select_topk_ties_mid_sizes(nb):
+    """Top-k at mid sizes with many ties (40 distinct scores)."""
+    rng = np.random.default_rng(nb)
+    s = rng.integers(0, 40, nb).astype(np.float32) / 4
+    for k in (1, nb // 5, nb // 2, nb - 1, nb):
+        _select_case(s, O.SELECT_TOPK, keep=k)
+
+
 def test_select_on_oracle_scores():
     """The realistic case: scores of a real workload (oracle's, rounded to fp32)."""
     w = synth.WORKLOADS["tiny"]
