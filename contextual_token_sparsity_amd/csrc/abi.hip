@@ -133,7 +133,7 @@ lemo_status lemo_block_scores(const lemo_bf16* q, const lemo_bf16* k, int n_toke
 
 size_t lemo_block_scores_batched_workspace(int n_batch, int n_tokens, int block) {
   if (n_batch <= 0 || n_tokens <= 0 || block <= 0) return 0;
-  const size_t nb = (size_t)((n_tokens + block - 1) / block);
+  const size_t nb = (size_t)lemo_nblocks(n_tokens, block);
   return lemo_align256((size_t)n_batch * nb * nb * sizeof(float));
 }
 
@@ -157,7 +157,7 @@ lemo_status lemo_block_scores_batched(const lemo_bf16* q, const lemo_bf16* k, in
           block);
   REQUIRE(head_reduce == LEMO_REDUCE_PAPER || n_heads <= 128, LEMO_ERR_UNSUPPORTED,
           "HEADMAX supports at most 128 heads (got %d)", n_heads);
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const long long ntq = (n_tokens + 127) / 128;
   const long long tiles = (flags & LEMO_SCORES_CAUSAL) ? ntq * (ntq + 1) / 2 : ntq * ntq;
   REQUIRE(n_batch * tiles <= (n_heads == 1 ? 0x7fffffffLL : kMaxWorkgroups), LEMO_ERR_UNSUPPORTED,
@@ -207,8 +207,8 @@ static lemo_status predict_checks(const lemo_bf16* x, int n_tokens, int d_model,
   REQUIRE(pow2(block) && block >= 2 && block <= 256, LEMO_ERR_UNSUPPORTED, "block %d (power of two, 2..256)", block);
   REQUIRE(d_model % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_model %d (multiple of 64 supported)", d_model);
   REQUIRE(rank % 32 == 0 && rank <= 256, LEMO_ERR_UNSUPPORTED, "rank %d (multiple of 32, at most 256)", rank);
-  REQUIRE((n_tokens + block - 1) / block <= 65535, LEMO_ERR_UNSUPPORTED, "%d blocks (at most 65535)",
-          (n_tokens + block - 1) / block);
+  REQUIRE(lemo_nblocks(n_tokens, block) <= 65535, LEMO_ERR_UNSUPPORTED, "%d blocks (at most 65535)",
+          lemo_nblocks(n_tokens, block));
   lemo_status st;
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
   REQUIRE(aligned16(u_q) && aligned16(v_q) && aligned16(u_k) && aligned16(v_k), LEMO_ERR_ALIGNMENT,
@@ -268,7 +268,7 @@ lemo_status lemo_token_embeddings(const lemo_bf16* x, int n_tokens, int d_model,
   if ((st = check_rows(x, ld_x, d_model, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, ld_x, "x")) != LEMO_OK) return st;
   if ((st = check_offsets(n_tokens, 2 * rank, "hidden layer")) != LEMO_OK) return st;
-  REQUIRE((n_tokens + 63) / 64 * (long long)((2 * rank + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
+  REQUIRE(lemo_nblocks(n_tokens, 64) * (long long)((2 * rank + 127) / 128) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED,
           "n_tokens %d: too many tiles for one launch", n_tokens);
   if ((st = check_rows(q_hat, ld_out, rank, "q_hat")) != LEMO_OK) return st;
   if ((st = check_rows(k_hat, ld_out, rank, "k_hat")) != LEMO_OK) return st;
@@ -388,7 +388,7 @@ lemo_status lemo_residual_recompute_capped(lemo_bf16* residual, int n_tokens, in
 
 size_t lemo_mlp_block_scores_workspace(int n_tokens, int width, int block) {
   if (n_tokens <= 0 || width <= 0 || block <= 0) return 0;
-  const size_t nb = (size_t)((n_tokens + block - 1) / block);
+  const size_t nb = (size_t)lemo_nblocks(n_tokens, block);
   return lemo_align256(nb * lemo_mlp_chunks(width) * sizeof(float));
 }
 
@@ -400,8 +400,8 @@ static lemo_status mlp_scores(const char* fn, const lemo_bf16* act, int ld_act, 
           "sizes must be positive (n_tokens=%d block=%d width=%d)", n_tokens, block, width);
   REQUIRE(width % 8 == 0, LEMO_ERR_ALIGNMENT, "width %d must be a multiple of 8", width);
   REQUIRE(lemo_mlp_chunks(width) <= 65535, LEMO_ERR_UNSUPPORTED, "width %d too large", width);
-  REQUIRE((n_tokens + block - 1) / block <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED, "%d blocks (at most %lld)",
-          (n_tokens + block - 1) / block, kMaxWorkgroups);
+  REQUIRE(lemo_nblocks(n_tokens, block) <= kMaxWorkgroups, LEMO_ERR_UNSUPPORTED, "%d blocks (at most %lld)",
+          lemo_nblocks(n_tokens, block), kMaxWorkgroups);
   lemo_status st;
   if ((st = check_rows(act, ld_act, width, up ? "gate" : "act")) != LEMO_OK) return st;
   if (up && (st = check_rows(up, ld_up, width, "up")) != LEMO_OK) return st;
@@ -438,7 +438,7 @@ lemo_status lemo_gather_linear(const lemo_bf16* x, int n_tokens, int d_in, int l
           n_tokens, block, d_in, d_out, cap_rows, pad_multiple);
   REQUIRE(d_in % 64 == 0, LEMO_ERR_UNSUPPORTED, "d_in %d (multiple of 64 supported)", d_in);
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
-  REQUIRE((cap_rows + 255LL) / 256 * ((d_out + 255) / 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
+  REQUIRE((long long)lemo_nblocks(cap_rows, 256) * lemo_nblocks(d_out, 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
           "cap_rows %d x d_out %d: more than %lld tiles of 256 x 256 for one launch", cap_rows, d_out,
           kMaxFusedWorkgroups);
   lemo_status st;
@@ -465,7 +465,7 @@ lemo_status lemo_linear_scatter(const lemo_bf16* a, int d_in, int ld_a, int cap_
   REQUIRE(d_out % 8 == 0, LEMO_ERR_ALIGNMENT, "d_out %d must be a multiple of 8", d_out);
   // the product covers min(cap_rows, n_tokens) rows (no more rows can be kept)
   const long long prod_rows = cap_rows < n_tokens ? cap_rows : n_tokens;
-  REQUIRE((prod_rows + 255) / 256 * ((d_out + 255) / 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
+  REQUIRE((prod_rows + 255) / 256 * lemo_nblocks(d_out, 256) <= kMaxFusedWorkgroups, LEMO_ERR_UNSUPPORTED,
           "%lld rows x d_out %d: more than %lld tiles of 256 x 256 for one launch", prod_rows, d_out,
           kMaxFusedWorkgroups);
   lemo_status st;

@@ -638,8 +638,8 @@ __global__ __launch_bounds__(pp::kThr, 1) void k_gemm_nt_pp(Args g, int lda, int
 
 // Grid of k_gemm_nt<., TM, TN, WAVES>: row tiles x column tiles, products in z.
 inline dim3 grid_for(int tile_rows, int tile_cols, int rows, int cols, int products, int& tm_count, int& tn_count) {
-  tm_count = (rows + tile_rows - 1) / tile_rows;
-  tn_count = (cols + tile_cols - 1) / tile_cols;
+  tm_count = lemo_nblocks(rows, tile_rows);
+  tn_count = lemo_nblocks(cols, tile_cols);
   return dim3(tm_count * tn_count, 1, products);
 }
 

@@ -114,3 +114,7 @@ hipError_t lemo_launch_mlp_scores(const uint16_t* act, int ld_act, const uint16_
 hipError_t lemo_launch_colsum(const float* m, int nb, float* out, hipStream_t stream, int n_batch = 1);
 
 static inline size_t lemo_align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Blocks of `block` rows covering n rows (n >= 0, block >= 1), formed without
+// the int overflow of n + block - 1 for n near INT_MAX.
+__host__ __device__ static inline int lemo_nblocks(int n, int block) { return n / block + (n % block != 0); }

@@ -103,11 +103,11 @@ __global__ __launch_bounds__(256) void k_mlp_final(const float* __restrict__ par
 
 }  // namespace
 
-int lemo_mlp_chunks(int width) { return (width + kChunkCols - 1) / kChunkCols; }
+int lemo_mlp_chunks(int width) { return lemo_nblocks(width, kChunkCols); }
 
 hipError_t lemo_launch_mlp_scores(const uint16_t* act, int ld_act, const uint16_t* up, int ld_up, int n_tokens,
                                   int width, int block, float* scores, void* workspace, hipStream_t stream) {
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const int n_chunks = lemo_mlp_chunks(width);
   float* partial = static_cast<float*>(workspace);
   const dim3 grid(nb, n_chunks);

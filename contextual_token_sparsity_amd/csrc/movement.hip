@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherArgs g, int n_tokens,
                                                      const int32_t* __restrict__ kept,
                                                      const int32_t* __restrict__ n_kept_p, int cap_rows,
                                                      int pad_multiple, int32_t* __restrict__ status) {
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
   const int n_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
                                                       const int32_t* __restrict__ n_kept_p,
                                                       const uint16_t* __restrict__ y, int ld_y, int y_rows,
                                                       int32_t* __restrict__ status) {
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const int nk = *n_kept_p;
   const bool bad_count = nk < 0 || nk > nb;
   const int all_rows = bad_count ? 0 : kept_rows(kept, nk, block, nb, n_tokens);
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(uint16_t* __restrict__ res
 // only known on the device, and a grid sized for every possible row leaves
 // most workgroups idle (each still reads n_kept).
 dim3 grid_for(int width, int max_rows) {
-  const int gx = (width / 8 + kThreads - 1) / kThreads;
+  const int gx = lemo_nblocks(width / 8, kThreads);
   const int gy = max(1, min(max_rows, kRowSlots));
   return dim3(gx, gy);
 }

@@ -271,7 +271,7 @@ struct Layout {
 };
 
 Layout layout(int n_tokens, int d_model, int block, int rank) {
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const int s = lemo_predict_splitk(nb, d_model, rank);
   Layout L;
   size_t off = 0;
@@ -341,7 +341,7 @@ hipError_t lemo_launch_predict(const uint16_t* x, int n_tokens, int d_model, int
                                const uint16_t* u_q, const uint16_t* v_q, const uint16_t* u_k,
                                const uint16_t* v_k, int rank, float* m_out, float* scores, void* workspace,
                                hipStream_t st) {
-  const int nb = (n_tokens + block - 1) / block;
+  const int nb = lemo_nblocks(n_tokens, block);
   const Layout L = layout(n_tokens, d_model, block, rank);
   char* ws = static_cast<char*>(workspace);
   uint16_t* xbar = reinterpret_cast<uint16_t*>(ws + L.xbar);

@@ -436,3 +436,17 @@ def test_headmax_head_limit(L):
     assert "128 heads" in lemo.lemo_last_error()
     assert bs(L, h=128, hd=64, ldq=128 * 64, ldk=128 * 64, mode=1, M=NULL, ws=NULL) == WS
     assert bs(L, h=129, hd=64, ldq=129 * 64, ldk=129 * 64, mode=0, M=NULL, ws=NULL) == WS
+
+
+def test_block_counts_near_int_max(L):
+    """Block and tile counts are formed without int overflow: sizes near
+    2^31 are refused as too large instead of wrapping to a negative count
+    that would pass the limits."""
+    big = (1 << 31) - 1
+    assert ps(L, n=big, b=256, ws=NULL) == UNSUP           # 8388608 blocks (at most 65535)
+    assert "8388608 blocks" in lemo.lemo_last_error()
+    assert L.lemo_mlp_block_scores(P, big, 8, 8, 2, P, P, 1 << 40, NULL) == UNSUP   # 2^30 blocks
+    assert L.lemo_mlp_block_scores_workspace(big, 8, 2) == (1 << 30) * 4
+    d_out = big - 7                                        # a multiple of 8: 8388608 column tiles
+    assert L.lemo_gather_linear(P, 1024, 64, 64, 64, P, P, P, d_out, 64, P, d_out, 256, 1, NULL, NULL) == UNSUP
+    assert "256 x 256" in lemo.lemo_last_error()
