@@ -199,52 +199,64 @@ __global__ __launch_bounds__(512) void k_project(const float* __restrict__ part,
 // ------------------------------------------- pair scores and column sums
 // A workgroup owns NC key blocks n; thread t walks the query blocks
 // m = t, t + 256, ...: M_hat[m][n] = max(0, q_hat[m] . k_hat[n]) (fp32 dot
-// in v order; q_hat read column-wise from its transposed copy, 64 values at
-// a time with every load of the round issued before the k_hat rows are
-// staged in LDS), written only when the caller asked for the block matrix,
-// and summed per thread in m order; the per-thread sums are then added in
-// a fixed order (a butterfly inside each wave, then the four waves in
-// order), so I_hat[n] is deterministic.
+// in v order; q_hat read column-wise from its transposed copy in rounds of 32
+// values, two rounds in flight: the next round's loads are issued before the
+// current round's products), written only when the caller asked for the
+// block matrix, and summed per thread in m order; the per-thread sums are
+// then added in a fixed order (a butterfly inside each wave, then the four
+// waves in order), so I_hat[n] is deterministic.  The k_hat rows are staged
+// in LDS while the first two rounds of q_hat loads are in flight.
 template <int NC>
 __global__ __launch_bounds__(256) void k_pair_colsum(const float* __restrict__ qhat_t, const float* __restrict__ khat,
                                                      int nb, int rank, float* __restrict__ M,
                                                      float* __restrict__ scores) {
+  constexpr int kRound = 32;
   __shared__ __attribute__((aligned(16))) float kt[NC][256];
   __shared__ float red[NC][4];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int n0 = blockIdx.x * NC;
+  const int nr = rank / kRound;   // rank is a multiple of 32
   float cs[NC] = {};
-  bool staged = false;
   for (int m0 = 0; m0 < nb; m0 += 256) {
     const int m = m0 + t;
     const float* qc = qhat_t + min(m, nb - 1);
+    float qa[kRound], qb[kRound];
+    // round rd of this thread's q_hat column (past the last round: the last
+    // round again, not used)
+    auto load_round = [&](float (&dst)[kRound], int rd) {
+      rd = min(rd, nr - 1);
+#pragma unroll
+      for (int j = 0; j < kRound; ++j) dst[j] = qc[(size_t)(kRound * rd + j) * nb];
+    };
+    load_round(qa, 0);
+    load_round(qb, 1);
+    if (m0 == 0) {   // uniform: every thread takes the first pass
+      for (int i = t; i < NC * rank; i += 256) {
+        const int n = i / rank, v = i % rank;
+        kt[n][v] = n0 + n < nb ? khat[(size_t)(n0 + n) * rank + v] : 0.f;
+      }
+      __syncthreads();
+    }
     float dot[NC] = {};
-    for (int v0 = 0; v0 < rank; v0 += 64) {
-      float q[64];
+    auto products = [&](const float (&q)[kRound], int rd) {
 #pragma unroll
-      for (int j = 0; j < 64; ++j)
-        if (v0 + j < rank) q[j] = qc[(size_t)(v0 + j) * nb];
-      if (!staged) {   // uniform: every thread reaches it in the same round
-        for (int i = t; i < NC * rank; i += 256) {
-          const int n = i / rank, v = i % rank;
-          kt[n][v] = n0 + n < nb ? khat[(size_t)(n0 + n) * rank + v] : 0.f;
-        }
-        __syncthreads();
-        staged = true;
-      }
+      for (int j = 0; j < kRound; j += 4) {
 #pragma unroll
-      for (int j = 0; j < 64; j += 4) {
-        if (v0 + j < rank) {   // rank is a multiple of 32
-#pragma unroll
-          for (int n = 0; n < NC; ++n) {
-            const float4 k4 = *reinterpret_cast<const float4*>(&kt[n][v0 + j]);
-            dot[n] = fmaf(q[j], k4.x, dot[n]);
-            dot[n] = fmaf(q[j + 1], k4.y, dot[n]);
-            dot[n] = fmaf(q[j + 2], k4.z, dot[n]);
-            dot[n] = fmaf(q[j + 3], k4.w, dot[n]);
-          }
+        for (int n = 0; n < NC; ++n) {
+          const float4 k4 = *reinterpret_cast<const float4*>(&kt[n][kRound * rd + j]);
+          dot[n] = fmaf(q[j], k4.x, dot[n]);
+          dot[n] = fmaf(q[j + 1], k4.y, dot[n]);
+          dot[n] = fmaf(q[j + 2], k4.z, dot[n]);
+          dot[n] = fmaf(q[j + 3], k4.w, dot[n]);
         }
       }
+    };
+    for (int rd = 0; rd < nr; rd += 2) {
+      products(qa, rd);
+      if (rd + 1 >= nr) break;
+      load_round(qa, rd + 2);
+      products(qb, rd + 1);
+      load_round(qb, rd + 3);
     }
     if (m < nb) {
 #pragma unroll
