@@ -257,7 +257,8 @@ def main():
     if "chain" in sec:
         out["chain_13b"] = chain_13b(stream, dev)
     if "select" in sec:
-        out["select_topk"] = select_topk(stream, dev)
+        out["select_topk"] = select_latency(stream, dev, "topk")
+        out["select_mean"] = select_latency(stream, dev, "mean")
     if "causal" in sec:
         out["causal_scores"] = causal_scores(q, k, N, H, hd, b, mode, stream, dev)
     if "headmax" in sec:
@@ -749,9 +750,10 @@ def chain_13b(stream, dev, reps=5):
             "token_layers_per_s": 4 * N / (chain_ms * 1e-3), "layers": layers_out, "dev_status": st}
 
 
-def select_topk(stream, dev):
-    """Latency of the top-k select (keep 30 %) at 256 and 8192 blocks on
-    seeded random scores: mean event time of 20 calls after a settle phase."""
+def select_latency(stream, dev, mode):
+    """Latency of the select at 256 and 8192 blocks on seeded random scores:
+    top-k keeping 30 %, or the mean threshold; mean event time of 20 calls
+    after a settle phase."""
     import torch
     from contextual_token_sparsity_amd import lemo, synth
     out = {}
@@ -760,9 +762,12 @@ def select_topk(stream, dev):
         s_ = torch.rand(nb, device=dev, generator=g)
         bufs = (torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.int32, device=dev),
                 torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
-        k = synth.keep_count(30, nb)
-        t = _mean_ms(lambda: lemo.lemo_select_mask(s_, lemo.SELECT_TOPK, keep_blocks=k, mask=bufs[0],
-                                                   kept_blocks=bufs[1], n_kept=bufs[2], threshold_used=bufs[3]),
+        if mode == "topk":
+            sel, kw = lemo.SELECT_TOPK, {"keep_blocks": synth.keep_count(30, nb)}
+        else:
+            sel, kw = lemo.SELECT_MEAN, {}
+        t = _mean_ms(lambda: lemo.lemo_select_mask(s_, sel, mask=bufs[0], kept_blocks=bufs[1], n_kept=bufs[2],
+                                                   threshold_used=bufs[3], **kw),
                      stream, reps=20)
         out[f"nb{nb}_us"] = t * 1e3
     return out
