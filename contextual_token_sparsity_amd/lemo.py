@@ -170,7 +170,10 @@ def lemo_block_scores(q, k, n_heads: int, head_dim: int, block: int, head_reduce
     if block <= 0:
         raise ValueError(f"block must be positive (got {block})")
     nb = n // block
-    _rows_within(k, n, 0, "k")
+    # the C side sees only the row stride: the columns the heads span must lie
+    # inside each operand (a narrow view of a wider matrix has ld >= width)
+    _rows_within(q, n, n_heads * head_dim, "q")
+    _rows_within(k, n, n_heads * head_dim, "k")
     if scores is None:
         scores = torch.empty(nb, dtype=torch.float32, device=q.device)
     _buf(scores, torch.float32, nb, "scores", q.device)
@@ -202,6 +205,9 @@ def lemo_block_scores_batched(q, k, n_heads: int, head_dim: int, block: int, hea
     B, n = q.shape[0], q.shape[1]
     if block <= 0:
         raise ValueError(f"block must be positive (got {block})")
+    for name, t in (("q", q), ("k", k)):
+        if t.shape[2] < n_heads * head_dim:
+            raise ValueError(f"{name} is {tuple(t.shape)}, {n_heads * head_dim} columns needed")
     nb = (n + block - 1) // block
     if scores is None:
         scores = torch.empty(B, nb, dtype=torch.float32, device=q.device)

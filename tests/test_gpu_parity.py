@@ -1580,6 +1580,13 @@ def test_binding_rejects_bad_buffers():
     with pytest.raises(ValueError, match="needed"):
         lemo.lemo_select_mask(torch.zeros(nb, device="cuda"), lemo.SELECT_MEAN,
                               kept_blocks=torch.zeros(nb - 1, dtype=torch.int32, device="cuda"))
+    # the heads must lie inside each operand's columns: a view of the last
+    # half of a wider matrix has a row stride that covers them, its columns do not
+    wide = dev(synth.random_bf16(rng, (n, 2 * h * hd)))
+    with pytest.raises(ValueError, match="needed"):
+        lemo.lemo_block_scores(wide[:, h * hd + 8:], wide[:, :h * hd], h, hd, b)
+    with pytest.raises(ValueError, match="columns needed"):
+        lemo.lemo_block_scores_batched(wide[:, h * hd + 8:], wide[:, :h * hd], h, hd, b)
     # the workspace holds nb*nb floats: a float32 tensor of that many elements suffices
     ws = torch.empty(lemo.lemo_block_scores_workspace(n, b) // 4, dtype=torch.float32, device="cuda")
     I, _ = lemo.lemo_block_scores(q, k, h, hd, b, workspace=ws)
