@@ -539,6 +539,14 @@ def check_select(o) -> list:
     mask, kept, nk, th = o.select_mask(m8, o.SELECT_MEAN)
     _fail(out, th == np.float32(np.mean(m8.astype(np.float64))), "mean threshold")
     _fail(out, np.array_equal(mask.astype(bool), m8 >= th), "mean mask")
+    # mean: the float64 sum runs in block order (the reading both sides take).
+    # 2^60 + 1 rounds to 2^60 in float64, so [2^60, 1, -2^60] averages to 0,
+    # while [2^60, -2^60, 1] averages to 1/3; an exact or reordered sum would
+    # give one value for both
+    big = 2.0 ** 60
+    th0 = o.select_mask(np.array([big, 1, -big], np.float32), o.SELECT_MEAN)[3]
+    th1 = o.select_mask(np.array([big, -big, 1], np.float32), o.SELECT_MEAN)[3]
+    _fail(out, th0 == 0.0 and th1 == np.float32(1.0 / 3.0), f"mean in block order: {th0} {th1}")
     # mean of scores that are not exact: the correctly rounded sum (math.fsum)
     # over nb, rounded to float32
     mask, kept, nk, th = o.select_mask(s, o.SELECT_MEAN)

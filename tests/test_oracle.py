@@ -79,6 +79,10 @@ MUTATIONS = [
      "        pass\n    return dst, n_pad > cap\n\n\ndef linear_scatter", [P.check_fused_movement]),
     ("threshold_strict", "keep = s >= theta\n    elif mode == SELECT_MEAN", "keep = s > theta\n    elif mode == SELECT_MEAN",
      [P.check_select]),
+    ("mean_exact_sum", "        for v in s:\n            total += float(v)", "        total = math.fsum(float(v) for v in s)",
+     [P.check_select]),
+    ("mean_reversed_order", "        for v in s:\n            total += float(v)", "        for v in s[::-1]:\n            total += float(v)",
+     [P.check_select]),
     ("topk_ties_high_index", "-float(s[c]) if not np.isnan(s[c]) else 0.0, c))",
      "-float(s[c]) if not np.isnan(s[c]) else 0.0, -c))", [P.check_select]),
     ("round_truncates", "r = np.rint(np.ldexp(ax, -qexp))", "r = np.floor(np.ldexp(ax, -qexp))",
