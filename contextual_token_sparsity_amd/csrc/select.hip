@@ -104,43 +104,54 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ s
     // non-finite score, or a wider range, one lane sums in block order.
     // Partial sums start at +0, as the sequential one does, so zeros of
     // either sign give the same +0.
+    // Up to 1024 blocks wave 0 alone reduces (lane l takes blocks l, l + 64,
+    // ...: one butterfly, no barrier); beyond that every wave takes a share
+    // and thread 0 adds the 16 wave sums.
+    const bool one_wave = nb <= 1024;   // uniform
     double part = 0.0, mag = 0.0;
     int lsb = 0x7fffffff;
     bool fin = true;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int c = tid + j * kThreads;
-      if (c < nb) {
+    if (!one_wave || wave == 0) {
+      const int stride = one_wave ? 64 : kThreads;
+      for (int c = tid; c < nb; c += stride) {
         const double v = (double)s[c];
         fin = fin && __builtin_isfinite(v);
         if (v != 0.0 && __builtin_isfinite(v)) lsb = min(lsb, lowest_bit(v));
         part += v;
         mag += fabs(v);
       }
-    }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      part += __shfl_xor(part, off, 64);
-      mag += __shfl_xor(mag, off, 64);
-      lsb = min(lsb, __shfl_xor(lsb, off, 64));
+      for (int off = 1; off < 64; off <<= 1) {
+        part += __shfl_xor(part, off, 64);
+        mag += __shfl_xor(mag, off, 64);
+        lsb = min(lsb, __shfl_xor(lsb, off, 64));
+      }
     }
     const bool wave_fin = __ballot(!fin) == 0ull;
-    if (lane == 0) {
-      wsum[wave] = part;
-      wmag[wave] = mag;
-      wlsb[wave] = lsb;
-      wfin[wave] = wave_fin ? 1 : 0;
+    if (!one_wave) {
+      if (lane == 0) {
+        wsum[wave] = part;
+        wmag[wave] = mag;
+        wlsb[wave] = lsb;
+        wfin[wave] = wave_fin ? 1 : 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (tid == 0) {
-      double total = 0.0, bound = 0.0;
-      int b = 0x7fffffff;
-      bool all_fin = true;
-      for (int w = 0; w < kWaves; ++w) {
-        total += wsum[w];
-        bound += wmag[w];
-        b = min(b, wlsb[w]);
-        all_fin = all_fin && wfin[w];
+      double total = part, bound = mag;
+      int b = lsb;
+      bool all_fin = wave_fin;
+      if (!one_wave) {
+        total = 0.0;
+        bound = 0.0;
+        b = 0x7fffffff;
+        all_fin = true;
+        for (int w = 0; w < kWaves; ++w) {
+          total += wsum[w];
+          bound += wmag[w];
+          b = min(b, wlsb[w]);
+          all_fin = all_fin && wfin[w];
+        }
       }
       // 2^(b + 52) as a float64 (b >= -149 for float32 inputs, so it is normal)
       const bool exact =
