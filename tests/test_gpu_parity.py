@@ -775,7 +775,7 @@ def test_select_mean_sum_paths():
     summed as a tree) and inputs whose sum in block order rounds (summed by one
     lane in that order) both give the oracle's threshold bit for bit."""
     rng = np.random.default_rng(11)
-    for nb in (3, 256, 1025, 8192):
+    for nb in (3, 256, 1024, 1025, 8192):   # one wave reduces up to 1024 blocks, 16 beyond
         # multiples of 2^-8 below 64, either sign: a span of at most 27 bits
         s = (rng.integers(-2 ** 14, 2 ** 14, nb) / 256.0).astype(np.float32)
         _select_case(s, O.SELECT_MEAN)
